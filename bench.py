@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the Differential Attention forward operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one fused prefill launch over the whole batch of the headline
+workload (causal_prefill_bf16: B4 H16 N2048, d64, dv128, bf16, causal), i.e.
+operand staging, both score contractions, both online softmaxes, both P.V
+contractions and the subtraction + GroupNorm epilogue.  Inputs are synthetic,
+seeded, and resident in HBM before timing starts.  The throughput counts
+4 (d + dv) flops per unmasked (query, key) pair (two Q.K^T and two P.V).
+
+The same run also times the decode kernels (split-K partials + merge) on the
+decode workload (B64 H32, one query against an 8192-entry KV cache) and
+reports them in "decode" as GB/s of algorithmic cache traffic, and times the
+fp64 CPU oracle on a bounded sample of the headline workload ("cpu_baseline").
+
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks: dense bf16 MFMA and HBM3E bandwidth
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "DiffAttn fwd TFLOP/s (prefill) and KV GB/s (decode), % of roofline"
+
+
+def _events_time(fn, steps: int):
+    """Runs fn() `steps` times between two events on the current stream; returns ms per call."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    stop.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def bench_prefill(w, steps: int, warmup: int):
+    import torch
+
+    import transformer_attention_diffattn_amd as da
+    import workloads
+
+    x = workloads.make_prefill(w, device="cuda")
+    out = torch.empty((w.B, w.H, w.nq, w.dv), dtype=w.torch_dtype, device="cuda")
+
+    def step():
+        da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], lambda_init=w.lambda_init,
+               causal=w.causal, eps=w.eps, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # wall clock over exactly `steps` steps, bracketed by synchronisations
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # per-launch device time from events on the launch stream
+    kern_ms = _events_time(step, steps)
+    del x, out
+    return wall_ms, kern_ms
+
+
+def bench_decode(w, steps: int, warmup: int):
+    import torch
+
+    import transformer_attention_diffattn_amd as da
+    import workloads
+
+    x = workloads.make_decode(w, device="cuda")
+    out = torch.empty((w.B, w.H, w.dv), dtype=w.torch_dtype, device="cuda")
+    splits = da.decode_default_splits(w.B, w.H, w.nk, w.d, w.dv)
+    ws_bytes = da.decode_workspace_size(w.B, w.H, w.nk, w.d, w.dv, splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"],
+                  lambda_init=w.lambda_init, eps=w.eps, out=out, workspace=ws,
+                  num_splits=splits)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    kern_ms = _events_time(step, steps)
+    del x, out, ws
+    torch.cuda.empty_cache()
+    return kern_ms, splits, ws_bytes
+
+
+def cpu_baseline(w, budget_s: float = 30.0):
+    """Times the fp64 oracle (as it is) head by head over the workload, stopping
+    after about budget_s seconds of compute or when every head is done; reports
+    the rate in the headline's unit (4 (d + dv) flops per unmasked pair)."""
+    import oracle
+    import workloads
+
+    x = workloads.make_prefill(w, device="cpu")
+    lam = x["lam"].numpy()
+    oracle.num_threads()  # load outside the timed region
+    heads, pairs, elapsed = 0, 0, 0.0
+    per_head = w.nq * (w.nq + 1) // 2 if w.causal else w.nq * w.nk
+    for b in range(w.B):
+        for h in range(w.H):
+            args = [x[k][b, h].double().numpy() for k in ("q1", "q2", "k1", "k2", "v")]
+            t0 = time.perf_counter()
+            oracle.head_rows(*args, None, causal=w.causal, lam=float(lam[h]),
+                             lambda_init=w.lambda_init, eps=w.eps)
+            elapsed += time.perf_counter() - t0
+            heads += 1
+            pairs += per_head
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    flops = 4 * (w.d + w.dv) * pairs
+    return {
+        "value": round(flops / elapsed / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} heads, all {w.nq} query rows each "
+                  f"({elapsed:.2f} s of fp64 compute, input upcast excluded)",
+        "tokens_per_s": round(heads * w.nq / elapsed, 1),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="causal_prefill_bf16")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this operator is built and timed on a single "
+              "MI355X (multi-GPU sharding is a design note only); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_attention_diffattn_amd as da
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    da.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    w = workloads.get(args.workload)
+    if w.kind != "prefill":
+        print("--workload must name a prefill workload", file=sys.stderr)
+        sys.exit(2)
+    wall_ms, kern_ms = bench_prefill(w, args.steps, args.warmup)
+    flops = w.exec_flops()
+    value = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.nq,
+                   "head_dim": w.d, "v_dim": w.dv, "causal": w.causal,
+                   "global_batch": w.B, "parallelism": "single GPU"},
+        "tokens_per_s": round(w.B * w.nq / (wall_ms * 1e-3), 1),
+        "formula_tflops": round(w.formula_flops() / (wall_ms * 1e-3) / 1e12, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_bf16_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "launch_ms": round(kern_ms, 4),
+            "flops_per_launch": flops,
+        },
+    }
+
+    if not args.no_decode:
+        wd = workloads.get("decode_bf16")
+        dec_steps = max(5, args.steps // 5)
+        dms, splits, ws_bytes = bench_decode(wd, dec_steps, max(2, args.warmup // 2))
+        nbytes = wd.algorithmic_bytes()
+        gbs = nbytes / (dms * 1e-3) / 1e9
+        rec["decode"] = {
+            "workload": wd.name,
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "ms_per_call": round(dms, 4),
+            "tokens_per_s": round(wd.B / (dms * 1e-3), 1),
+            "splits": splits,
+            "workspace_bytes": ws_bytes,
+            "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel (+ merge)",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_call": nbytes},
+        }
+
+    if not args.no_cpu:
+        cb = cpu_baseline(w)
+        cb["cpu"] = _cpu_model()
+        rec["cpu_baseline"] = cb
+
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

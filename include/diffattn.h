@@ -1,0 +1,142 @@
+/*
+ * diffattn.h -- C ABI of the MI355X (gfx950) Differential Attention forward
+ * operator.
+ *
+ * The operator (iloveeagents.com, "Mathematical Formula"; llmbytes.dev, "How
+ * Differential Attention Cancels Common-Mode Noise", steps 1-4), per batch
+ * entry b, head h and query row i:
+ *
+ *   A1 = softmax(Q1 K1^T / sqrt(d)),  A2 = softmax(Q2 K2^T / sqrt(d))
+ *   D  = (A1 - lambda[h] * A2) V                                 (dv channels)
+ *   out = (1 - lambda_init) * (D - mean(D)) / sqrt(var(D) + eps)
+ *
+ * where d is the query/key head dimension, mean and var are the population
+ * moments of the head's dv channels of that row (GroupNorm with one group per
+ * head, no affine parameters), and a causal mask, when asked for, lets query i
+ * see keys 0..i in both maps.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are device memory owned by the caller, contiguous, row-major,
+ *     [batch][heads][seq][channels] with the channel dimension unit-stride.
+ *     Base pointers must be 16-byte aligned.  The library keeps no pointer
+ *     after a call returns and never frees caller memory.
+ *   - q1, q2, k1, k2, v and out share one element type (DIFFATTN_F32 or
+ *     DIFFATTN_BF16).  All arithmetic is fp32; the output is rounded once
+ *     (round-to-nearest-even) to the element type.
+ *   - lambda is a device array of `heads` fp32 values.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; faults during execution surface at the caller's next
+ *     synchronisation.
+ *   - Every argument is checked before any HIP call.  On an error status
+ *     nothing is launched and no memory is written.  Nothing is printed and
+ *     nothing aborts.
+ *   - out must not overlap any input.
+ *   - Calls are thread-safe; the library holds no state besides a per-device
+ *     cache of the compute-unit count.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIFFATTN_ABI_VERSION 1
+
+/* element types */
+#define DIFFATTN_F32 0
+#define DIFFATTN_BF16 1
+
+/* status codes */
+#define DIFFATTN_OK 0
+#define DIFFATTN_ERR_INVALID 1     /* NULL pointer, size < 1, misaligned pointer,
+                                      non-finite scalar, eps < 0 */
+#define DIFFATTN_ERR_UNSUPPORTED 2 /* well formed but outside the support matrix */
+#define DIFFATTN_ERR_WORKSPACE 3   /* decode workspace missing or too small */
+#define DIFFATTN_ERR_HIP 4         /* the HIP runtime refused the launch */
+
+/* flags */
+#define DIFFATTN_FLAG_PRE_NORM 1u  /* write D itself: skip the GroupNorm and the
+                                      (1 - lambda_init) scale (for checks) */
+
+/*
+ * Problem sizes.  Supported (head_dim, v_dim) pairs: (32, 64), (64, 128),
+ * (128, 256), for both element types.  Sizes are limited to
+ * batch * heads <= 2^31 - 1 and seq_q, seq_k <= 2^30.
+ */
+typedef struct {
+    int32_t batch;    /* B >= 1 */
+    int32_t heads;    /* H >= 1 */
+    int32_t seq_q;    /* query rows per head (decode: must be 1) */
+    int32_t seq_k;    /* keys per head; decode: the longest valid cache length */
+    int32_t head_dim; /* d: channels of Q1, Q2, K1, K2 */
+    int32_t v_dim;    /* dv: channels of V and of the output */
+    int32_t dtype;    /* DIFFATTN_F32 or DIFFATTN_BF16 */
+    float eps;        /* GroupNorm epsilon, >= 0 (added to the variance) */
+    uint32_t flags;   /* DIFFATTN_FLAG_* */
+} diffattn_dims;
+
+/* The version this library was built with (DIFFATTN_ABI_VERSION). */
+int diffattn_abi_version(void);
+
+/* A static, human-readable name for a status code. */
+const char* diffattn_status_string(int status);
+
+/*
+ * Prefill (fused forward over all query rows).
+ *   q1, q2 [B][H][seq_q][d]; k1, k2 [B][H][seq_k][d]; v [B][H][seq_k][dv];
+ *   out [B][H][seq_q][dv]; lambda [H] fp32 (device).
+ *   causal != 0 applies the mask j <= i to both maps and needs seq_q == seq_k.
+ * Allocates nothing.  Returns a DIFFATTN_* status.
+ */
+int diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
+                 const void* v, const float* lambda, float lambda_init, int causal,
+                 void* out, const diffattn_dims* dims, void* stream);
+
+/*
+ * Decode: one new query token per (b, h) against a KV cache.  Every cached
+ * position of the sequence is visible (the cache already holds the current
+ * token), so no mask applies.
+ *   q1, q2 [B][H][d]; k1_cache, k2_cache [B][H][kv_capacity][d];
+ *   v_cache [B][H][kv_capacity][dv]; out [B][H][dv]; lambda [H] (device).
+ *   dims->seq_q must be 1; dims->seq_k = L is the cache length used, with
+ *   1 <= L <= kv_capacity.
+ *   kv_lens: NULL (every sequence has length L) or a device int32 array [B]
+ *   of per-sequence lengths; each is clamped to [0, L], and a sequence of
+ *   length 0 gets an all-zero output row.
+ *   num_splits: how many pieces each sequence's cache is cut into (split-K);
+ *   0 lets the library choose.  With more than one piece, partial results go
+ *   to `workspace` (device memory of at least
+ *   diffattn_decode_workspace_size(dims, num_splits) bytes, 16-byte aligned,
+ *   owned by the caller, contents on entry ignored) and a second kernel merges
+ *   them.  workspace may be NULL when that size is 0.
+ * Allocates nothing.  Returns a DIFFATTN_* status.
+ */
+int diffattn_decode(const void* q1, const void* q2, const void* k1_cache,
+                    const void* k2_cache, const void* v_cache, int32_t kv_capacity,
+                    const int32_t* kv_lens, const float* lambda, float lambda_init,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    int32_t num_splits, const diffattn_dims* dims, void* stream);
+
+/*
+ * The split count diffattn_decode uses for num_splits = 0 on the current
+ * device (queries the device's compute-unit count once).  Returns a value
+ * >= 1, or 0 if dims is invalid or the device cannot be queried.
+ */
+int32_t diffattn_decode_default_splits(const diffattn_dims* dims);
+
+/*
+ * Workspace bytes diffattn_decode needs for these sizes and num_splits
+ * (0 = the default count).  0 when no workspace is needed (one split) or
+ * when the arguments are invalid.
+ */
+size_t diffattn_decode_workspace_size(const diffattn_dims* dims, int32_t num_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

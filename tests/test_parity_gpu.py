@@ -1,0 +1,295 @@
+"""Parity of the HIP path with the fp64 oracle (GPU).
+
+Every call goes through the C ABI (via the ctypes binding).  Tolerances:
+fp32 inputs, max |gpu - oracle| <= 1e-4; bf16 inputs, every element within
+1.5e-2 + 2e-2 * |oracle|.  The oracle reads the very values the GPU read
+(bf16 and fp32 upcast exactly to fp64).
+
+Small cases compare every output element; they span several 128-row query
+tiles and 64-key tiles with ragged tails.  The full-size workloads compare
+sampled rows (tile edges, first and last rows, needle rows, random rows)
+that the oracle computes one by one, in the launch configuration the
+benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_diffattn_amd as da
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def assert_close(gpu, ref, dtype, what=""):
+    g = gpu.detach().to("cpu", torch.float64).numpy() if isinstance(gpu, torch.Tensor) else gpu
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    err = np.abs(g - ref)
+    if dtype == torch.float32:
+        worst = float(err.max()) if err.size else 0.0
+        assert worst <= 1e-4, f"{what}: max abs err {worst:.3e} > 1e-4"
+    else:
+        bound = 1.5e-2 + 2e-2 * np.abs(ref)
+        ratio = err / bound
+        i = np.unravel_index(np.argmax(ratio), ratio.shape) if ratio.size else None
+        assert ratio.size == 0 or ratio.max() <= 1.0, (
+            f"{what}: element {i} gpu {g[i]:.5f} oracle {ref[i]:.5f} "
+            f"(max abs err {err.max():.3e})")
+
+
+def _to(x, dev=DEV):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def _custom(B, H, nq, nk, d, dv, dtype, causal, seed, dist="normal", lam=("uniform", 0.2, 0.9)):
+    return workloads.Workload("custom", "prefill", B=B, H=H, nq=nq, nk=nk, d=d, dv=dv,
+                              dtype=dtype, causal=causal, dist=dist, lam=lam, seed=seed)
+
+
+def _run_prefill_full_compare(w, pre_norm=False):
+    x = workloads.make_prefill(w, device="cpu")
+    xg = _to(x)
+    out = da.fwd(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"],
+                 lambda_init=w.lambda_init, causal=w.causal, eps=w.eps, pre_norm=pre_norm)
+    torch.cuda.synchronize()
+    ref = oracle.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=w.causal,
+                     lambda_init=w.lambda_init, eps=w.eps, pre_norm=pre_norm)
+    return out, ref
+
+
+# --------------------------------------------------------------------------
+# small prefill shapes, every element
+# --------------------------------------------------------------------------
+
+SMALL_N = [1, 7, 64, 129, 300]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dims", da.SUPPORTED_DIMS, ids=lambda t: f"d{t[0]}dv{t[1]}")
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("n", SMALL_N)
+def test_prefill_small(dtype, dims, causal, n):
+    d, dv = dims
+    w = _custom(2, 3, n, n, d, dv, dtype, causal, seed=1000 + n + d)
+    out, ref = _run_prefill_full_compare(w)
+    assert_close(out, ref, w.torch_dtype, f"{dtype} d{d} n{n} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nq,nk", [(70, 300), (300, 5), (1, 513), (200, 64)])
+def test_prefill_rectangular_noncausal(dtype, nq, nk):
+    w = _custom(1, 2, nq, nk, 64, 128, dtype, False, seed=nq * 7 + nk)
+    out, ref = _run_prefill_full_compare(w)
+    assert_close(out, ref, w.torch_dtype, f"{dtype} nq{nq} nk{nk}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_pre_norm_output(dtype):
+    w = _custom(1, 2, 200, 200, 64, 128, dtype, True, seed=77)
+    out, ref = _run_prefill_full_compare(w, pre_norm=True)
+    assert_close(out, ref, w.torch_dtype, "pre-norm D")
+
+
+def test_tiny_noncausal_f32_workload():
+    w = workloads.get("tiny_noncausal_f32")
+    out, ref = _run_prefill_full_compare(w)
+    assert_close(out, ref, torch.float32, w.name)
+
+
+# --------------------------------------------------------------------------
+# identities of the operator, through the kernels
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_value_ones_gives_one_minus_lambda(dtype):
+    w = _custom(1, 4, 150, 150, 64, 128, dtype, True, seed=5)
+    x = _to(workloads.make_prefill(w, device="cpu"))
+    v = torch.ones_like(x["v"])
+    d = da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], v, x["lam"], causal=True, pre_norm=True)
+    want = (1 - x["lam"]).view(1, -1, 1, 1).expand_as(d).to(torch.float64)
+    tol = 1e-5 if dtype == "f32" else 1.5e-2
+    assert float((d.double() - want).abs().max()) <= tol
+    out = da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], v, x["lam"], causal=True)
+    assert float(out.double().abs().max()) <= (1e-5 if dtype == "f32" else 2e-2)
+
+
+@pytest.mark.parametrize("dims", da.SUPPORTED_DIMS, ids=lambda t: f"d{t[0]}")
+def test_identical_maps_cancel_exactly(dims):
+    d, dv = dims
+    w = _custom(2, 2, 257, 257, d, dv, "bf16", True, seed=9)
+    x = _to(workloads.make_prefill(w, device="cpu"))
+    one = torch.ones(2, device=DEV)
+    pre = da.fwd(x["q1"], x["q1"], x["k1"], x["k1"], x["v"], one, causal=True, pre_norm=True)
+    out = da.fwd(x["q1"], x["q1"], x["k1"], x["k1"], x["v"], one, causal=True)
+    assert float(pre.abs().max()) == 0.0
+    assert float(out.abs().max()) == 0.0
+
+
+def test_causal_row0_closed_form():
+    w = _custom(1, 3, 96, 96, 64, 128, "bf16", True, seed=12)
+    x = _to(workloads.make_prefill(w, device="cpu"))
+    out = da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=True)
+    lam = x["lam"].double().view(-1, 1)
+    Dd = (1 - lam) * x["v"][0, :, 0].double()
+    ref = 0.2 * (Dd - Dd.mean(1, keepdim=True)) / torch.sqrt(
+        Dd.var(1, unbiased=False, keepdim=True) + 1e-5)
+    assert_close(out[0, :, 0], ref.cpu().numpy(), torch.bfloat16, "row 0")
+
+
+def test_deterministic_and_canary():
+    w = _custom(2, 4, 333, 333, 64, 128, "bf16", True, seed=31)
+    x = _to(workloads.make_prefill(w, device="cpu"))
+    n = 2 * 4 * 333 * 128
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[:n].view(2, 4, 333, 128)
+    da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=True, out=out)
+    first = out.clone()
+    for _ in range(3):
+        da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=True, out=out)
+        assert torch.equal(out, first)
+    assert bool((buf[n:] == 7.0).all())
+
+
+# --------------------------------------------------------------------------
+# full-size prefill workloads, sampled rows
+# --------------------------------------------------------------------------
+
+def _sample_rows(n, rng, extra=()):
+    base = {0, 1, 63, 64, 127, 128, 129, n // 2, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1}
+    base |= set(int(e) for e in extra)
+    base |= set(rng.integers(0, n, 6).tolist())
+    return sorted(r for r in base if 0 <= r < n)
+
+
+def _check_sampled(w, x, out, heads, rows_for):
+    for (b, h) in heads:
+        rows = rows_for(b, h)
+        ref = oracle.head_rows(x["q1"][b, h], x["q2"][b, h], x["k1"][b, h], x["k2"][b, h],
+                               x["v"][b, h], rows, causal=w.causal, lam=float(x["lam"][h]),
+                               lambda_init=w.lambda_init, eps=w.eps)
+        assert_close(out[b, h, rows], ref, w.torch_dtype, f"{w.name} b{b} h{h}")
+
+
+@pytest.mark.parametrize("name", ["causal_prefill_bf16", "long_needles_bf16", "large_head_bf16"])
+def test_full_size_prefill_sampled(name):
+    w = workloads.get(name)
+    xg = workloads.make_prefill(w, device=DEV)
+    out = da.fwd(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"],
+                 lambda_init=w.lambda_init, causal=w.causal, eps=w.eps)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    x = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in xg.items()}
+    del xg
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(7)
+    plans = workloads.needle_plan(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if len(heads) > 24:
+        pick = rng.choice(len(heads), 24, replace=False)
+        heads = [heads[i] for i in sorted(pick)]
+
+    def rows_for(b, h):
+        extra = plans[b * w.H + h][1] if plans else ()
+        return _sample_rows(w.nq, rng, extra)
+
+    _check_sampled(w, x, out, heads, rows_for)
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+
+def _custom_decode(B, H, L, d, dv, dtype, seed):
+    return workloads.Workload("custom_decode", "decode", B=B, H=H, nq=1, nk=L, d=d, dv=dv,
+                              dtype=dtype, causal=False, lam=("uniform", 0.3, 0.8), seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dims", da.SUPPORTED_DIMS, ids=lambda t: f"d{t[0]}")
+@pytest.mark.parametrize("L", [1, 5, 64, 200, 1000])
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_decode_small(dtype, dims, L, splits):
+    d, dv = dims
+    w = _custom_decode(3, 2, L, d, dv, dtype, seed=L + d)
+    x = workloads.make_decode(w, device="cpu")
+    xg = _to(x)
+    out = da.decode(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"],
+                    num_splits=splits)
+    ref = oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"])
+    assert_close(out, ref, w.torch_dtype, f"decode {dtype} d{d} L{L} splits{splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_ragged_lengths(splits):
+    w = _custom_decode(5, 2, 700, 64, 128, "bf16", seed=3)
+    x = workloads.make_decode(w, device="cpu")
+    xg = _to(x)
+    lens = torch.tensor([700, 1, 0, 333, 129], dtype=torch.int32)
+    out = da.decode(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"],
+                    kv_lens=lens.to(DEV), num_splits=splits).cpu()
+    for b in range(5):
+        L = int(lens[b])
+        if L == 0:
+            assert float(out[b].abs().max()) == 0.0
+            continue
+        ref = oracle.decode(x["q1"][b:b + 1], x["q2"][b:b + 1], x["k1"][b:b + 1],
+                            x["k2"][b:b + 1], x["v"][b:b + 1], x["lam"], kv_len=L)
+        assert_close(out[b:b + 1], ref, torch.bfloat16, f"ragged b{b} L{L}")
+
+
+def test_decode_inside_larger_cache():
+    w = _custom_decode(2, 3, 512, 64, 128, "bf16", seed=4)
+    x = workloads.make_decode(w, device="cpu")
+    xg = _to(x)
+    out = da.decode(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"], kv_len=300,
+                    num_splits=2)
+    ref = oracle.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], kv_len=300)
+    assert_close(out, ref, torch.bfloat16, "kv_len 300 of 512")
+
+
+def test_decode_equals_last_row_of_causal_prefill():
+    w = _custom(2, 4, 777, 777, 64, 128, "bf16", True, seed=21)
+    x = _to(workloads.make_prefill(w, device="cpu"))
+    pre = da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=True,
+                 pre_norm=True)
+    dec = da.decode(x["q1"][:, :, -1].contiguous(), x["q2"][:, :, -1].contiguous(), x["k1"],
+                    x["k2"], x["v"], x["lam"], num_splits=3, pre_norm=True)
+    diff = (pre[:, :, -1].double() - dec.double()).abs().max()
+    assert float(diff) <= 1e-2
+
+
+def test_decode_split_count_invariance():
+    w = _custom_decode(2, 4, 4096, 64, 128, "bf16", seed=8)
+    x = _to(workloads.make_decode(w, device="cpu"))
+    outs = [da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], num_splits=s,
+                      pre_norm=True).double() for s in (1, 2, 5, 16, 32)]
+    for o in outs[1:]:
+        assert float((o - outs[0]).abs().max()) <= 1e-4
+    again = da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], num_splits=5,
+                      pre_norm=True).double()
+    assert torch.equal(again, outs[2])
+
+
+def test_full_size_decode_sampled():
+    w = workloads.get("decode_bf16")
+    xg = workloads.make_decode(w, device=DEV)
+    out = da.decode(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"],
+                    lambda_init=w.lambda_init, eps=w.eps).cpu()
+    rng = np.random.default_rng(11)
+    heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 40), rng.integers(0, w.H, 40))]
+    heads += [(0, 0), (w.B - 1, w.H - 1)]
+    lam = xg["lam"].cpu()
+    for b, h in heads:
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        ref = oracle.decode(sl(xg["q1"]), sl(xg["q2"]), sl(xg["k1"]), sl(xg["k2"]),
+                            sl(xg["v"]), lam[h:h + 1], lambda_init=w.lambda_init, eps=w.eps)
+        assert_close(out[b:b + 1, h:h + 1], ref, torch.bfloat16, f"decode b{b} h{h}")
+    del xg
+    torch.cuda.empty_cache()

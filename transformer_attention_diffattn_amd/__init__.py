@@ -1,0 +1,231 @@
+"""MI355X (gfx950) Differential Attention forward: Python binding.
+
+A thin ctypes layer over ``libdiffattn.so`` (the HIP kernels behind the C ABI
+in ``include/diffattn.h``).  It only checks and marshals arguments: every step
+of the operator runs in the library's kernels.  PyTorch supplies device memory
+and the current stream.  There is no fallback: if the library is not built,
+every call raises.
+
+The operator (iloveeagents.com, "Mathematical Formula"; llmbytes.dev, "How
+Differential Attention Cancels Common-Mode Noise", steps 1-4):
+
+    out = (1 - lambda_init) * GroupNorm_h((softmax(Q1 K1^T / sqrt(d))
+                                           - lambda_h softmax(Q2 K2^T / sqrt(d))) V)
+
+with one GroupNorm group per head over its dv channels (population variance,
+eps inside the square root, no affine parameters).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence, Union
+
+import torch
+
+__all__ = [
+    "fwd", "decode", "decode_workspace_size", "decode_default_splits", "abi_version",
+    "library_path", "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libdiffattn.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "diffattn.h")
+
+SUPPORTED_DIMS = ((32, 64), (64, 128), (128, 256))
+F32, BF16 = 0, 1
+FLAG_PRE_NORM = 1
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_q", ctypes.c_int32),
+        ("seq_k", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("eps", ctypes.c_float), ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m transformer_attention_diffattn_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        DP = ctypes.POINTER(Dims)
+        L.diffattn_abi_version.restype = I
+        L.diffattn_abi_version.argtypes = []
+        L.diffattn_status_string.restype = ctypes.c_char_p
+        L.diffattn_status_string.argtypes = [I]
+        L.diffattn_fwd.restype = I
+        L.diffattn_fwd.argtypes = [P, P, P, P, P, P, F, I, P, DP, P]
+        L.diffattn_decode.restype = I
+        L.diffattn_decode.argtypes = [P, P, P, P, P, ctypes.c_int32, P, P, F, P, P,
+                                      ctypes.c_size_t, ctypes.c_int32, DP, P]
+        L.diffattn_decode_default_splits.restype = ctypes.c_int32
+        L.diffattn_decode_default_splits.argtypes = [DP]
+        L.diffattn_decode_workspace_size.restype = ctypes.c_size_t
+        L.diffattn_decode_workspace_size.argtypes = [DP, ctypes.c_int32]
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/diffattn.h declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def abi_version() -> int:
+    return int(lib().diffattn_abi_version())
+
+
+def _check(status: int):
+    if status != OK:
+        msg = lib().diffattn_status_string(status).decode()
+        if status in (ERR_INVALID, ERR_UNSUPPORTED):
+            raise ValueError(f"diffattn: {msg} (status {status})")
+        raise DiffAttnError(status, f"diffattn: {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _stream_ptr(device: torch.device) -> Optional[int]:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _lam_tensor(lam, H: int, device) -> torch.Tensor:
+    if isinstance(lam, torch.Tensor):
+        t = lam.to(device=device, dtype=torch.float32).reshape(-1)
+    else:
+        t = torch.as_tensor(lam, dtype=torch.float32).reshape(-1).to(device)
+    if t.numel() == 1:
+        t = t.expand(H)
+    if t.numel() != H:
+        raise ValueError(f"lambda must have 1 or {H} values, got {t.numel()}")
+    return t.contiguous()
+
+
+def _require(ok: bool, msg: str):
+    if not ok:
+        raise ValueError(msg)
+
+
+def fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
+        v: torch.Tensor, lam: Union[float, Sequence[float], torch.Tensor],
+        lambda_init: float = 0.8, causal: bool = True, eps: float = 1e-5,
+        out: Optional[torch.Tensor] = None, pre_norm: bool = False) -> torch.Tensor:
+    """Fused prefill.  q1, q2 [B,H,Nq,d]; k1, k2 [B,H,Nk,d]; v [B,H,Nk,dv]; all
+    bf16 or all fp32, contiguous, on one GPU.  lam: scalar or [H].  Returns
+    out [B,H,Nq,dv] in the input dtype.  pre_norm=True returns
+    D = (A1 - lam A2) V without the GroupNorm and scale."""
+    ts = (q1, q2, k1, k2, v)
+    _require(all(t.is_cuda for t in ts), "inputs must be GPU tensors")
+    _require(all(t.device == q1.device for t in ts), "inputs must share one device")
+    _require(all(t.dtype == q1.dtype for t in ts), "inputs must share one dtype")
+    _require(all(t.dim() == 4 for t in ts), "inputs must be [B,H,N,dim]")
+    _require(all(t.is_contiguous() for t in ts), "inputs must be contiguous")
+    B, H, Nq, d = q1.shape
+    Nk, dv = k1.shape[2], v.shape[3]
+    _require(q2.shape == (B, H, Nq, d), "q2 shape must equal q1 shape")
+    _require(k1.shape == (B, H, Nk, d) and k2.shape == (B, H, Nk, d), "k1/k2 shape mismatch")
+    _require(v.shape == (B, H, Nk, dv), "v shape mismatch")
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=q1.dtype, device=q1.device)
+    _require(out.shape == (B, H, Nq, dv) and out.dtype == q1.dtype and out.is_contiguous()
+             and out.device == q1.device, "out must be a contiguous [B,H,Nq,dv] tensor")
+    lam_t = _lam_tensor(lam, H, q1.device)
+    dims = Dims(B, H, Nq, Nk, d, dv, _dtype_code(q1), float(eps),
+                FLAG_PRE_NORM if pre_norm else 0)
+    st = lib().diffattn_fwd(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
+                            v.data_ptr(), lam_t.data_ptr(), float(lambda_init), int(bool(causal)),
+                            out.data_ptr(), ctypes.byref(dims), _stream_ptr(q1.device))
+    _check(st)
+    return out
+
+
+def _decode_dims(B, H, L, d, dv, dtype_code, eps, pre_norm) -> Dims:
+    return Dims(B, H, 1, L, d, dv, dtype_code, float(eps), FLAG_PRE_NORM if pre_norm else 0)
+
+
+def decode_default_splits(B: int, H: int, L: int, d: int, dv: int) -> int:
+    """Split count the library picks for these sizes on the current device."""
+    return int(lib().diffattn_decode_default_splits(
+        ctypes.byref(_decode_dims(B, H, L, d, dv, BF16, 1e-5, False))))
+
+
+def decode_workspace_size(B: int, H: int, L: int, d: int, dv: int, num_splits: int = 0) -> int:
+    return int(lib().diffattn_decode_workspace_size(
+        ctypes.byref(_decode_dims(B, H, L, d, dv, BF16, 1e-5, False)), int(num_splits)))
+
+
+def decode(q1: torch.Tensor, q2: torch.Tensor, k1_cache: torch.Tensor, k2_cache: torch.Tensor,
+           v_cache: torch.Tensor, lam, lambda_init: float = 0.8, kv_len: Optional[int] = None,
+           kv_lens: Optional[torch.Tensor] = None, num_splits: int = 0, eps: float = 1e-5,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           pre_norm: bool = False) -> torch.Tensor:
+    """KV-cache decode.  q1, q2 [B,H,d]; caches [B,H,cap,d] / [B,H,cap,dv].
+    kv_len: cache length used (default: cap); kv_lens: optional int32 [B] of
+    per-sequence lengths (clamped to [0, kv_len]).  Returns out [B,H,dv]."""
+    ts = (q1, q2, k1_cache, k2_cache, v_cache)
+    _require(all(t.is_cuda for t in ts), "inputs must be GPU tensors")
+    _require(all(t.device == q1.device for t in ts), "inputs must share one device")
+    _require(all(t.dtype == q1.dtype for t in ts), "inputs must share one dtype")
+    _require(all(t.is_contiguous() for t in ts), "inputs must be contiguous")
+    _require(q1.dim() == 3 and k1_cache.dim() == 4 and v_cache.dim() == 4, "bad ranks")
+    B, H, d = q1.shape
+    cap, dv = k1_cache.shape[2], v_cache.shape[3]
+    _require(q2.shape == (B, H, d), "q2 shape must equal q1 shape")
+    _require(k1_cache.shape == (B, H, cap, d) and k2_cache.shape == (B, H, cap, d),
+             "k caches shape mismatch")
+    _require(v_cache.shape == (B, H, cap, dv), "v cache shape mismatch")
+    L = cap if kv_len is None else int(kv_len)
+    if kv_lens is not None:
+        _require(kv_lens.is_cuda and kv_lens.dtype == torch.int32 and kv_lens.numel() == B
+                 and kv_lens.is_contiguous(), "kv_lens must be a contiguous int32 [B] GPU tensor")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q1.dtype, device=q1.device)
+    _require(out.shape == (B, H, dv) and out.dtype == q1.dtype and out.is_contiguous(),
+             "out must be a contiguous [B,H,dv] tensor")
+    lam_t = _lam_tensor(lam, H, q1.device)
+    dims = _decode_dims(B, H, L, d, dv, _dtype_code(q1), eps, pre_norm)
+    need = int(lib().diffattn_decode_workspace_size(ctypes.byref(dims), int(num_splits)))
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib().diffattn_decode(q1.data_ptr(), q2.data_ptr(), k1_cache.data_ptr(),
+                               k2_cache.data_ptr(), v_cache.data_ptr(), cap,
+                               kv_lens.data_ptr() if kv_lens is not None else None,
+                               lam_t.data_ptr(), float(lambda_init), out.data_ptr(), ws_ptr,
+                               ws_bytes, int(num_splits), ctypes.byref(dims),
+                               _stream_ptr(q1.device))
+    _check(st)
+    return out

@@ -34,7 +34,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_prefill", "make_decode", "make"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_prefill", "make_decode", "make", "needle_plan"]
 
 
 @dataclass(frozen=True)
@@ -203,6 +203,17 @@ def _plant_needles(q1: torch.Tensor, k1: torch.Tensor, plan, cos: float) -> None
         gv = gv / gv.norm()
         norm = k1[j].float().norm()
         k1[j] = (norm * (cos * u + math.sqrt(1.0 - cos * cos) * gv)).to(k1.dtype)
+
+
+def needle_plan(w: Workload):
+    """The needle positions make_prefill plants for workload w, per head
+    (flattened b*H + h): a list of (key positions, query positions, gaussian
+    vectors).  Empty when the workload has no needles."""
+    if not w.needles:
+        return []
+    aux = np.random.default_rng(_children(w)[-1])
+    _lambdas(w, aux)  # same draw order as make_prefill
+    return _needle_plan(w, aux, w.nq, w.nk)
 
 
 def make_prefill(w: Workload, device: str | torch.device = "cpu", seed: Optional[int] = None):
