@@ -139,6 +139,31 @@ def cpu_baseline(w, budget_s: float = 30.0):
     }
 
 
+COPY_BYTES = 1 << 30
+
+
+def _traffic(kernel: str):
+    """Scaled HBM bytes per launch from the committed rocprofv3 counter summary
+    of this kernel, or None when there is none or the kernel source changed."""
+    import profile_kernels
+
+    rec = profile_kernels.load(kernel)
+    return None if rec is None else rec["traffic_bytes_per_launch"]
+
+
+def copy_calibration():
+    """A plain elementwise copy (dst = src * 1) reading and writing COPY_BYTES."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -158,6 +183,9 @@ def main():
     ap.add_argument("--workload", default="causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain fp32 copy of 1 GiB (3 times), the reference the "
+                         "HBM byte counters are scaled by")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -176,6 +204,9 @@ def main():
         sys.exit(2)
     da.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        copy_calibration()
 
     w = workloads.get(args.workload)
     if w.kind != "prefill":
@@ -210,7 +241,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": _traffic("prefill_bf16_kernel") if w.name == "causal_prefill_bf16" else None,
             "launch_ms": round(kern_ms, 4),
             "flops_per_launch": flops,
         },
@@ -232,7 +263,8 @@ def main():
             "workspace_bytes": ws_bytes,
             "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel (+ merge)",
                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": _traffic("decode_partial_kernel"),
                          "bytes_per_call": nbytes},
         }
 

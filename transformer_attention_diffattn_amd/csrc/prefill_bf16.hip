@@ -8,20 +8,38 @@
 //
 // Work decomposition
 //   One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
-//   wave owns 32 rows.  K1, K2 and V stream through LDS in tiles of 64 keys,
-//   double-buffered: the next tile's global loads are issued into registers
-//   before the current tile's math and written to the other LDS buffer after
-//   it, so one barrier per tile suffices.
+//   wave owns 32 rows.  K1, K2 and V stream through a 3-stage LDS ring in tiles
+//   of 32 keys.  A kernel needs more than 256 registers per lane here, so there
+//   is one wave per SIMD and the overlap of matrix and vector work has to come
+//   from inside the wave.  Iteration j of the key loop is software-pipelined:
+//     step 0  row maxima of tile j's scores, rare rescale (see below);
+//     step 1  MFMA: scores of tile j+1        | VALU: probabilities of tile j
+//     step 2  MFMA: P.V of tile j (map 1)     | VALU: probabilities (map 2)
+//     step 3  MFMA: P.V of tile j (map 2)     | LDS store of tile j+2, global
+//                                               loads of tile j+3, masking
+//   (for dv = 256 steps 2 and 3 are one P.V step after both maps' softmax, so
+//   that each V operand is read from LDS once without holding 64 registers).
+//   Tile j+1 must already be in LDS while tile j is consumed, hence 3 stages;
+//   one barrier per tile.  The steady state is branch-free apart from the
+//   rescale test, so the compiler can interleave the two pipes.
 //
 // Per tile and wave, on MFMA v_mfma_f32_32x32x16_bf16:
-//   S_k^T = K_k Q_k^T          (keys on the M axis, the wave's queries on N),
+//   S_k^T = K_k Q_k^T          (keys on the M axis, the wave's 32 queries on N),
 //   O_k^T = alpha_k O_k^T + V^T P_k^T   for k = 1, 2.
-//   Computing the transposed score tile puts every query in one lane pair
-//   (lanes l and l+32), so the row max and row sum of the online softmax are
-//   in-lane reductions plus one exchange, and the alpha rescale of O^T is a
-//   per-lane scalar.  The two maps keep separate (max, sum, O) states; the
-//   lambda-weighted subtraction happens once, in the epilogue, followed by the
-//   per-head GroupNorm over the dv channels and the (1 - lambda_init) scale.
+//   With the transposed score tile every query lives in one lane pair (lanes
+//   l and l+32), so online-softmax row statistics are in-lane reductions plus
+//   one exchange, and the rescale of O^T is a per-lane scalar.  The two maps
+//   keep separate (max, sum, O) states; the lambda-weighted subtraction happens
+//   once, in the epilogue, followed by the per-head GroupNorm over the dv
+//   channels and the (1 - lambda_init) scale.
+//
+// Online softmax with a lazy maximum: the running maximum m of a row only
+// moves when a new score exceeds it by more than kRescaleLog2 (in log2 units).
+// Until then probabilities are taken against the stale m and may reach
+// 2^kRescaleLog2; the sum l and O share that m, so O / l is unchanged.  The
+// O rescale (the only VALU work proportional to dv) therefore runs only when
+// some row of the wave moves its maximum by that much, which after the first
+// tile is rare.  It multiplies the accumulators where they live, in AGPRs.
 //
 // Operand layouts (32x32x16 MFMA; lane l, lh = l / 32, l32 = l % 32):
 //   A operand: row l32, k-slots 8*lh .. 8*lh+7;  B operand: column l32, the same
@@ -30,15 +48,21 @@
 //   keys (or channels) to k-slots gives the right contraction.
 //   The score tile's A operand loads key row swap23(l32) (bits 2 and 3 of the
 //   row index exchanged), which makes accumulator register r of lane l hold
-//   key 16*(r/8) + 8*lh + r%8 of the 32-key block.  Registers 8c .. 8c+7 of the
-//   score accumulator then form, after conversion to bf16, exactly the B
-//   operand P^T for keys 16c + 8*lh .. +7, matching an A operand that reads 8
-//   consecutive keys of a V^T row: the probabilities never leave registers.
+//   key 16*(r/8) + 8*lh + r%8 of the tile.  Registers 8c .. 8c+7, converted to
+//   bf16, are then exactly the B operand P^T for keys 16c + 8*lh .. +7: the
+//   probabilities never leave registers.
+//   The P.V A operand (V^T: channel rows, key k-slots) comes from a row-major
+//   V tile through ds_read_b64_tr_b16, the gfx950 transposing LDS read: within
+//   each 16-lane group, lane i receives element i%4 of the 8-byte pieces that
+//   lanes 4e + i/4 (e = 0..3) address.  Lane j = 4e + r of a group addresses
+//   key e (of 4 consecutive keys) at channel base + 4r, so lane i gets channel
+//   base + i of those 4 keys; two such reads give the 8 keys of a k-slot half.
 //
-// LDS per stage: K1 and K2 row-major [64][d + 8] (the pad keeps 16-byte row
-// reads conflict-free), V transposed [dv][64] with its 16-byte chunks XOR-
-// swizzled by (row + row/8) & 7 so both the transposing 8-byte writes and the
-// 16-byte operand reads spread over the banks.
+// LDS per stage: K1 and K2 row-major [32][d + 8] (the pad keeps the 16-byte
+// operand reads conflict-free), V row-major [32][dv + 32] (a 64-byte pad puts
+// the 4 rows a half-wave of transposing reads touches in distinct banks).
+// Global loads clamp the key index to the last valid row instead of branching;
+// scores of keys past the end are masked, so the clamped rows contribute 0.
 
 #include "internal.h"
 
@@ -48,32 +72,39 @@ namespace diffattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
-constexpr int kBr = 128;  // query rows per workgroup
-constexpr int kBc = 64;   // keys per tile
+constexpr int kWaves = 4;
+constexpr int kBc = 32;                 // keys per tile
+constexpr float kRescaleLog2 = 8.0f;    // lazy-maximum slack, log2 units
 
 template <int D, int DV>
-struct Layout {
-    static constexpr int kKStride = D + 8;  // elements per K row in LDS
+struct Cfg {
+    static constexpr int kBr = kWaves * 32;
+    static constexpr int kStages = 3;
+    static constexpr bool kSplitPV = DV <= 128;  // P.V per map, V operands kept
+    // d <= 64 carries the raw score accumulators across iterations and masks a
+    // working copy; d = 128 (no spare registers) masks in place and copies
+    static constexpr bool kCarryRaw = D <= 64;
+    static constexpr int kKStride = D + 8;
+    static constexpr int kVStride = DV + 32;
     static constexpr int kKElems = kBc * kKStride;
-    static constexpr int kVtElems = DV * kBc;
-    static constexpr int kStage = 2 * kKElems + kVtElems;  // bf16 elements per stage
-    static constexpr int kKChunks = D / 8;                   // 16-byte chunks per K row
-    static constexpr int kKLoads = kBc * kKChunks / kThreads;
-    static constexpr int kVGroups = (kBc / 4) * (DV / 8);   // 4 keys x 8 channels each
-    static constexpr int kVLoads = (kVGroups + kThreads - 1) / kThreads;
-    static_assert(kBc * kKChunks % kThreads == 0, "K tile must split evenly");
+    static constexpr int kVElems = kBc * kVStride;
+    static constexpr int kStage = 2 * kKElems + kVElems;  // bf16 elements per stage
+    static constexpr int kKChunks = kBc * D / 8;           // 16-byte chunks per K tile
+    static constexpr int kVChunks = kBc * DV / 8;
+    static constexpr int kKLoads = (kKChunks + kThreads - 1) / kThreads;
+    static constexpr int kVLoads = (kVChunks + kThreads - 1) / kThreads;
 };
 
 __device__ __forceinline__ int swap23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-
-__device__ __forceinline__ int vt_swizzle(int row) { return (row + (row >> 3)) & 7; }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
@@ -84,10 +115,76 @@ __device__ __forceinline__ float diff_of_products(float a, float b, float c, flo
     return a * b - c * d;
 }
 
+__device__ __forceinline__ float max16(const f32x16& s) {
+    float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+    float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    float c = fmaxf(fmaxf(s[6], s[7]), s[8]);
+    float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
+}
+
+// Multiplies every accumulator of o by alpha in place.  The accumulators live
+// in AGPRs; doing the read-multiply-write here keeps the compiler from holding
+// a VGPR copy of all of them around this rarely taken path.
+template <int NDB>
+__device__ __forceinline__ void scale_acc(f32x16 (&o)[NDB], float alpha) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x = o[db][r];
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(alpha));
+            o[db][r] = x;
+        }
+    }
+}
+
+// Moves the running maximum of one map when some row needs it (lazy rule).
+template <int NDB>
+__device__ __forceinline__ void maybe_rescale(float mx, float& m, float& l, f32x16 (&o)[NDB]) {
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2)) {
+        const float mrow = fmaxf(mx, xor32(mx));
+        const float mnew = fmaxf(m, mrow);
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        l *= alpha;
+        scale_acc<NDB>(o, alpha);
+    }
+}
+
+// Probabilities of one map: p = 2^(s * scale - base), summed into l and
+// packed to bf16 B operands (registers 8kb .. 8kb+7 per 16 keys).
+__device__ __forceinline__ void probabilities(const f32x16& s, float sl2, float base, float& l,
+                                              bf16x8 (&pb)[2]) {
+    float sum0 = 0.f, sum1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kb + e], sl2, -base));
+            if (e & 1)
+                sum1 += p;
+            else
+                sum0 += p;
+            pb[kb][e] = (__bf16)p;
+        }
+    }
+    l += sum0 + sum1;
+}
+
 template <int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
-    using LY = Layout<D, DV>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * LY::kStage];
+    using C = Cfg<D, DV>;
+    constexpr int NDB = DV / 32;
+    constexpr int NKB = D / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::kStages * C::kStage];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -97,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 
     // longest causal tiles first: the first B*H blocks take the last query tile
     const int BH = a.B * a.H;
-    const int nqt = (a.Nq + kBr - 1) / kBr;
+    const int nqt = (a.Nq + C::kBr - 1) / C::kBr;
     const int t = blockIdx.x / BH;
     const int bh = blockIdx.x - t * BH;
     const int qt = CAUSAL ? (nqt - 1 - t) : t;
@@ -110,13 +207,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     const uint16_t* gv = (const uint16_t*)a.v + (size_t)bh * a.Nk * DV;
     __bf16* gout = (__bf16*)a.out + (size_t)bh * a.Nq * DV;
 
-    const int qrow0 = qt * kBr + wave * 32;  // first query row of this wave
-    const int qrow = qrow0 + l32;            // this lane's query row
+    const int wq0 = qt * C::kBr + wave * 32;  // first query row of this wave
+    const int qrow = wq0 + l32;               // this lane's query row
 
     // Q fragments as B operands: column = query, k-slots = channels 16kb + 8lh ..
-    bf16x8 qf1[D / 16], qf2[D / 16];
+    bf16x8 qf1[NKB], qf2[NKB];
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
         if (qrow < a.Nq) {
             qf1[kb] = *(const bf16x8*)(gq1 + (size_t)qrow * D + 16 * kb + 8 * lh);
             qf2[kb] = *(const bf16x8*)(gq2 + (size_t)qrow * D + 16 * kb + 8 * lh);
@@ -127,205 +224,198 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     }
 
     const int nkt_all = (a.Nk + kBc - 1) / kBc;
-    const int nkt = CAUSAL ? min(nkt_all, (qt * kBr + kBr + kBc - 1) / kBc) : nkt_all;
+    const int nkt = CAUSAL ? min(nkt_all, (qt * C::kBr + C::kBr + kBc - 1) / kBc) : nkt_all;
+    const int last_key = a.Nk - 1;
 
-    u32x4 rk1[LY::kKLoads], rk2[LY::kKLoads], rv[LY::kVLoads][4];
+    u32x4 rk1[C::kKLoads], rk2[C::kKLoads], rv[C::kVLoads];
 
+    // global -> registers; key indices clamp to the last row (masked later)
     auto load_tile = [&](int kt) {
         const int key0 = kt * kBc;
 #pragma unroll
-        for (int i = 0; i < LY::kKLoads; ++i) {
+        for (int i = 0; i < C::kKLoads; ++i) {
             const int c = tid + i * kThreads;
-            const int row = c / LY::kKChunks, ch = c % LY::kKChunks;
-            const int key = key0 + row;
-            if (key < a.Nk) {
-                rk1[i] = *(const u32x4*)(gk1 + (size_t)key * D + ch * 8);
-                rk2[i] = *(const u32x4*)(gk2 + (size_t)key * D + ch * 8);
-            } else {
-                rk1[i] = u32x4{0, 0, 0, 0};
-                rk2[i] = u32x4{0, 0, 0, 0};
-            }
+            const int key = min(key0 + c / (D / 8), last_key);
+            const int ch = c % (D / 8);
+            rk1[i] = *(const u32x4*)(gk1 + (size_t)key * D + ch * 8);
+            rk2[i] = *(const u32x4*)(gk2 + (size_t)key * D + ch * 8);
         }
 #pragma unroll
-        for (int i = 0; i < LY::kVLoads; ++i) {
-            const int g = tid + i * kThreads;
-            if (g < LY::kVGroups) {
-                const int rg = g / (DV / 8), cc = g % (DV / 8);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = key0 + 4 * rg + r;
-                    rv[i][r] = key < a.Nk ? *(const u32x4*)(gv + (size_t)key * DV + cc * 8)
-                                          : u32x4{0, 0, 0, 0};
-                }
-            }
+        for (int i = 0; i < C::kVLoads; ++i) {
+            const int c = tid + i * kThreads;
+            const int key = min(key0 + c / (DV / 8), last_key);
+            const int ch = c % (DV / 8);
+            rv[i] = *(const u32x4*)(gv + (size_t)key * DV + ch * 8);
         }
     };
 
     auto store_tile = [&](int buf) {
-        uint16_t* k1s = smem + buf * LY::kStage;
-        uint16_t* k2s = k1s + LY::kKElems;
-        uint16_t* vts = k2s + LY::kKElems;
+        uint16_t* k1s = smem + buf * C::kStage;
+        uint16_t* k2s = k1s + C::kKElems;
+        uint16_t* vs = k2s + C::kKElems;
 #pragma unroll
-        for (int i = 0; i < LY::kKLoads; ++i) {
+        for (int i = 0; i < C::kKLoads; ++i) {
             const int c = tid + i * kThreads;
-            const int row = c / LY::kKChunks, ch = c % LY::kKChunks;
-            *(u32x4*)(k1s + row * LY::kKStride + ch * 8) = rk1[i];
-            *(u32x4*)(k2s + row * LY::kKStride + ch * 8) = rk2[i];
+            if (C::kKChunks % kThreads == 0 || c < C::kKChunks) {
+                const int row = c / (D / 8), ch = c % (D / 8);
+                *(u32x4*)(k1s + row * C::kKStride + ch * 8) = rk1[i];
+                *(u32x4*)(k2s + row * C::kKStride + ch * 8) = rk2[i];
+            }
         }
 #pragma unroll
-        for (int i = 0; i < LY::kVLoads; ++i) {
-            const int g = tid + i * kThreads;
-            if (g < LY::kVGroups) {
-                const int rg = g / (DV / 8), cc = g % (DV / 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int col = 8 * cc + e;
-                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    // channel `col` of keys 4rg .. 4rg+3, two keys per dword
-                    const uint32_t lo = __builtin_amdgcn_perm(rv[i][1][e >> 1], rv[i][0][e >> 1], sel);
-                    const uint32_t hi = __builtin_amdgcn_perm(rv[i][3][e >> 1], rv[i][2][e >> 1], sel);
-                    const int off = col * kBc + (((rg >> 1) ^ vt_swizzle(col)) << 3) + ((rg & 1) << 2);
-                    *(u32x2*)(vts + off) = u32x2{lo, hi};
-                }
+        for (int i = 0; i < C::kVLoads; ++i) {
+            const int c = tid + i * kThreads;
+            if (C::kVChunks % kThreads == 0 || c < C::kVChunks) {
+                const int row = c / (DV / 8), ch = c % (DV / 8);
+                *(u32x4*)(vs + row * C::kVStride + ch * 8) = rv[i];
             }
         }
     };
 
-    const float NEG_INF = -INFINITY;
-    const float sl2 = a.scale_log2;
-    float m1 = NEG_INF, m2 = NEG_INF;  // running max of scaled log2 scores
-    float l1 = 0.f, l2 = 0.f;          // running sums, this lane's half of the keys
-    f32x16 o1[DV / 32], o2[DV / 32];
+    const int krow = swap23(l32);
+    auto scores = [&](int buf, f32x16& s1, f32x16& s2) {
+        const uint16_t* k1s = smem + buf * C::kStage;
+        const uint16_t* k2s = k1s + C::kKElems;
+        s1 = f32x16{};
+        s2 = f32x16{};
 #pragma unroll
-    for (int db = 0; db < DV / 32; ++db) {
+        for (int kb = 0; kb < NKB; ++kb) {
+            const bf16x8 ka1 = *(const bf16x8*)(k1s + krow * C::kKStride + 16 * kb + 8 * lh);
+            const bf16x8 ka2 = *(const bf16x8*)(k2s + krow * C::kKStride + 16 * kb + 8 * lh);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf1[kb], s1, 0, 0, 0);
+            s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2, qf2[kb], s2, 0, 0, 0);
+        }
+    };
+
+    // keys past the end, and keys after the query under the causal mask, to -inf
+    auto mask = [&](int kt, f32x16& s1, f32x16& s2) {
+        const int key0 = kt * kBc;
+        const bool need = (CAUSAL && key0 + kBc - 1 > wq0) || (key0 + kBc > a.Nk);
+        if (need) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 16 * (r >> 3) + 8 * lh + (r & 7);
+                const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
+                s1[r] = ok ? s1[r] : -INFINITY;
+                s2[r] = ok ? s2[r] : -INFINITY;
+            }
+        }
+    };
+
+    // per-lane pieces of the transposing V read: key e of 4, channel offset 4r
+    const int vg = lane >> 4;
+    const int v_lane_off = (8 * (vg >> 1) + ((lane & 15) >> 2)) * C::kVStride +
+                           16 * (vg & 1) + 4 * (lane & 3);
+    auto v_operand = [&](int buf, int db, int kb) {
+        const uint16_t* vp = smem + buf * C::kStage + 2 * C::kKElems + v_lane_off +
+                             16 * kb * C::kVStride + 32 * db;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)vp);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(vp + 4 * C::kVStride));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    const float sl2 = a.scale_log2;
+    float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
+    f32x16 o1[NDB], o2[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
         o1[db] = f32x16{};
         o2[db] = f32x16{};
     }
 
+    // prologue: tiles 0 and 1 into LDS, tile 2 into registers, scores of tile 0
     load_tile(0);
     store_tile(0);
+    load_tile(1);
+    store_tile(1);
     __syncthreads();
+    load_tile(2);
+    // n1, n2: score accumulators of the next tile; s1, s2: tile j's scores
+    f32x16 n1, n2, s1, s2;
+    if constexpr (C::kCarryRaw) {
+        scores(0, n1, n2);
+    } else {
+        scores(0, s1, s2);
+        mask(0, s1, s2);
+    }
 
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        const bool has_next = kt + 1 < nkt;
-        if (has_next) load_tile(kt + 1);
+    int bj = 0;  // stage of tile j; tile j+1 is in (bj+1)%3, tile j+2 goes to (bj+2)%3
+    for (int j = 0; j < nkt; ++j) {
+        const int bn = bj == 2 ? 0 : bj + 1;
+        const int bw = bn == 2 ? 0 : bn + 1;
 
-        const int key0 = kt * kBc;
-        // a wave whose rows all precede the tile's first key has nothing to do
-        const bool active = !CAUSAL || key0 <= qrow0 + 31;
-        if (active) {
-            const uint16_t* k1s = smem + buf * LY::kStage;
-            const uint16_t* k2s = k1s + LY::kKElems;
-            const uint16_t* vts = k2s + LY::kKElems;
+        if constexpr (C::kCarryRaw) {
+            s1 = n1;
+            s2 = n2;
+            mask(j, s1, s2);
+        }
 
-            f32x16 s1[2], s2[2];
+        // step 0: row maxima of tile j and the rare rescale
+        maybe_rescale<NDB>(max16(s1) * sl2, m1, l1, o1);
+        maybe_rescale<NDB>(max16(s2) * sl2, m2, l2, o2);
+        const float base1 = m1 == -INFINITY ? 0.f : m1;
+        const float base2 = m2 == -INFINITY ? 0.f : m2;
+
+        // step 1: scores of tile j+1 on MFMA while the VALU turns tile j into P
+        scores(bn, n1, n2);
+        bf16x8 p1[2], p2[2];
+        probabilities(s1, sl2, base1, l1, p1);
+
+        if constexpr (C::kSplitPV) {
+            // step 2: P.V for map 1 while map 2's probabilities are formed
+            bf16x8 va[NDB][2];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                s1[sb] = f32x16{};
-                s2[sb] = f32x16{};
-                const int krow = 32 * sb + swap23(l32);
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                for (int kb = 0; kb < D / 16; ++kb) {
-                    const bf16x8 ka1 = *(const bf16x8*)(k1s + krow * LY::kKStride + 16 * kb + 8 * lh);
-                    const bf16x8 ka2 = *(const bf16x8*)(k2s + krow * LY::kKStride + 16 * kb + 8 * lh);
-                    s1[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf1[kb], s1[sb], 0, 0, 0);
-                    s2[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2, qf2[kb], s2[sb], 0, 0, 0);
+                for (int kb = 0; kb < 2; ++kb) {
+                    va[db][kb] = v_operand(bj, db, kb);
+                    o1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb], p1[kb], o1[db], 0, 0, 0);
                 }
             }
-
-            // mask keys past the end, and keys after the query under the causal mask
-            const bool need_mask = (CAUSAL && key0 + kBc - 1 > qrow0) || (key0 + kBc > a.Nk);
-            if (need_mask) {
+            probabilities(s2, sl2, base2, l2, p2);
+            // step 3: P.V for map 2 while the tile traffic goes on
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + 32 * sb + 16 * (r >> 3) + 8 * lh + (r & 7);
-                        const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
-                        if (!ok) {
-                            s1[sb][r] = NEG_INF;
-                            s2[sb][r] = NEG_INF;
-                        }
-                    }
-                }
+                for (int kb = 0; kb < 2; ++kb)
+                    o2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb], p2[kb], o2[db], 0, 0, 0);
             }
-
-            float mx1 = NEG_INF, mx2 = NEG_INF;
+        } else {
+            probabilities(s2, sl2, base2, l2, p2);
+            // step 2: P.V for both maps, each V operand read once
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    mx1 = fmaxf(mx1, s1[sb][r]);
-                    mx2 = fmaxf(mx2, s2[sb][r]);
-                }
-            }
-            mx1 = fmaxf(mx1, xor32(mx1));
-            mx2 = fmaxf(mx2, xor32(mx2));
-
-            const float mn1 = fmaxf(m1, mx1 * sl2);
-            const float mn2 = fmaxf(m2, mx2 * sl2);
-            const float base1 = mn1 == NEG_INF ? 0.f : mn1;
-            const float base2 = mn2 == NEG_INF ? 0.f : mn2;
-            const float al1 = __builtin_amdgcn_exp2f(m1 - base1);
-            const float al2 = __builtin_amdgcn_exp2f(m2 - base2);
-            m1 = mn1;
-            m2 = mn2;
-
-            float rs1 = 0.f, rs2 = 0.f;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[sb][r], sl2, -base1));
-                    const float p2 = __builtin_amdgcn_exp2f(fmaf(s2[sb][r], sl2, -base2));
-                    s1[sb][r] = p1;
-                    s2[sb][r] = p2;
-                    rs1 += p1;
-                    rs2 += p2;
-                }
-            }
-            l1 = fmaf(l1, al1, rs1);
-            l2 = fmaf(l2, al2, rs2);
-
-#pragma unroll
-            for (int db = 0; db < DV / 32; ++db) {
-                o1[db] *= al1;
-                o2[db] *= al2;
-            }
-
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                bf16x8 p1b, p2b;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p1b[e] = (__bf16)s1[kb >> 1][8 * (kb & 1) + e];
-                    p2b[e] = (__bf16)s2[kb >> 1][8 * (kb & 1) + e];
-                }
-#pragma unroll
-                for (int db = 0; db < DV / 32; ++db) {
-                    const int vrow = 32 * db + l32;
-                    const bf16x8 va = *(const bf16x8*)(vts + vrow * kBc +
-                                                       (((2 * kb + lh) ^ vt_swizzle(vrow)) << 3));
-                    o1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1b, o1[db], 0, 0, 0);
-                    o2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2b, o2[db], 0, 0, 0);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 va = v_operand(bj, db, kb);
+                    o1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1[kb], o1[db], 0, 0, 0);
+                    o2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2[kb], o2[db], 0, 0, 0);
                 }
             }
         }
 
-        if (has_next) store_tile(buf ^ 1);
+        store_tile(bw);      // tile j+2 (stale and unused once past the end)
+        load_tile(j + 3);    // clamped rows once past the end
+        if constexpr (!C::kCarryRaw) mask(j + 1, n1, n2);
         __syncthreads();
+        if constexpr (!C::kCarryRaw) {
+            s1 = n1;
+            s2 = n2;
+        }
+        bj = bn;
     }
 
     // epilogue: D = O1/l1 - lambda O2/l2, then GroupNorm over the dv channels
-    l1 += xor32(l1);
-    l2 += xor32(l2);
     const float lam = a.lam[h];
-    const float c1 = 1.f / l1;
-    const float c2 = lam / l2;
+    const float L1 = l1 + xor32(l1);
+    const float L2 = l2 + xor32(l2);
+    const float c1 = 1.f / L1;
+    const float c2 = lam / L2;
     float dsum = 0.f;
 #pragma unroll
-    for (int db = 0; db < DV / 32; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float dval = diff_of_products(o1[db][r], c1, o2[db][r], c2);
@@ -338,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         const float mean = dsum * (1.f / DV);
         float vsum = 0.f;
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float c = o1[db][r] - mean;
@@ -349,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         const float var = vsum * (1.f / DV);
         const float scale = (1.f - a.lambda_init) / sqrtf(var + a.eps);
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o1[db][r] = (o1[db][r] - mean) * scale;
         }
@@ -358,10 +448,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     if (qrow < a.Nq) {
         __bf16* orow = gout + (size_t)qrow * DV;
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                 bf16x4 w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w[e] = (__bf16)o1[db][4 * g + e];
@@ -373,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 
 template <int D, int DV>
 hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
-    const int nqt = (a.Nq + kBr - 1) / kBr;
+    const int nqt = (a.Nq + Cfg<D, DV>::kBr - 1) / Cfg<D, DV>::kBr;
     const dim3 grid((unsigned)((int64_t)nqt * a.B * a.H));
     PrefillArgs copy = a;
     void* args[] = {&copy};
