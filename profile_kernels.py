@@ -87,6 +87,21 @@ def _find(out: str, sub: str, suffix: str) -> str:
     return sorted(hits)[0]
 
 
+def _bench_ms_in_trace(out: str, kernel: str):
+    """The per-launch time bench.py measured with events inside the traced run."""
+    try:
+        with open(os.path.join(out, "trace.log")) as f:
+            lines = [l for l in f if l.startswith("{")]
+        rec = json.loads(lines[-1])
+    except (OSError, IndexError, ValueError):
+        return None
+    if kernel == "prefill_bf16_kernel":
+        return rec["roofline"]["launch_ms"]
+    if kernel == "decode_partial_kernel" and "decode" in rec:
+        return rec["decode"]["ms_per_call"]
+    return None
+
+
 def _kernel_stats(out: str):
     rows = {}
     with open(_find(out, "trace", "kernel_stats.csv")) as f:
@@ -142,6 +157,7 @@ def summarize(out: str) -> None:
             continue
         w = workloads.get(wname)
         fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        bench_ms = _bench_ms_in_trace(out, kern)
         traffic = int(round((fk * f_factor + wk * w_factor) * 1024))
         rec = {
             "kernel": kern, "workload": wname, "calls": int(st["Calls"]),
@@ -153,6 +169,7 @@ def summarize(out: str) -> None:
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
             "source": src, "source_sha256": source_sha(src),
+            "bench_event_ms_in_traced_run": bench_ms,
         }
         lines = [
             f"# {kern} on {wname}",
@@ -171,6 +188,8 @@ def summarize(out: str) -> None:
             "| quantity | value |",
             "|---|---|",
             f"| launches traced | {rec['calls']} |",
+            f"| bench.py event-timed launch in the same traced run | "
+            f"{'n/a' if bench_ms is None else f'{bench_ms * 1e3:.1f} us'} |",
             f"| average duration | {rec['avg_ns'] / 1e3:.1f} us (min {rec['min_ns'] / 1e3:.1f}, "
             f"max {rec['max_ns'] / 1e3:.1f}) |",
             f"| FETCH_SIZE per dispatch | {fk:,.1f} KiB |",
