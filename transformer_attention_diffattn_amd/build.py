@@ -19,7 +19,12 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libdiffattn.so")
-SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_bf16_wide.hip", "prefill_f32.hip", "decode.hip"]
+# Per-source extra flags.  The narrow-head prefill kernel keeps its score
+# accumulators in ordinary VGPRs, where the softmax reads them without a copy
+# out of the accumulation registers; the compiler's default heuristic would
+# put every matrix accumulator in AGPRs.
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -39,7 +44,7 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

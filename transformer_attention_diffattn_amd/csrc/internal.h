@@ -48,6 +48,8 @@ struct DecodeArgs {
 // the supported pairs; the callers have checked that.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
                                hipStream_t stream);
+hipError_t launch_prefill_bf16_wide(const PrefillArgs& a, int d, int dv, bool causal,
+                                    hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);

@@ -1,4 +1,5 @@
-// Fused Differential Attention prefill for bf16 inputs on gfx950 (CDNA4).
+// Fused Differential Attention prefill for bf16 inputs on gfx950 (CDNA4),
+// head_dim 32 or 64 (head_dim 128 is in prefill_bf16_wide.hip).
 //
 // Operator: the DiffAttn formula (iloveeagents.com, "Mathematical Formula")
 // with the GroupNorm and (1 - lambda_init) scale of step 4 on llmbytes.dev
@@ -8,20 +9,20 @@
 //
 // Work decomposition
 //   One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
-//   wave owns 32 rows.  K1, K2 and V stream through a 3-stage LDS ring in tiles
-//   of 32 keys.  A kernel needs more than 256 registers per lane here, so there
-//   is one wave per SIMD and the overlap of matrix and vector work has to come
-//   from inside the wave.  Iteration j of the key loop is software-pipelined:
-//     step 0  row maxima of tile j's scores, rare rescale (see below);
-//     step 1  MFMA: scores of tile j+1        | VALU: probabilities of tile j
-//     step 2  MFMA: P.V of tile j (map 1)     | VALU: probabilities (map 2)
-//     step 3  MFMA: P.V of tile j (map 2)     | LDS store of tile j+2, global
-//                                               loads of tile j+3, masking
-//   (for dv = 256 steps 2 and 3 are one P.V step after both maps' softmax, so
-//   that each V operand is read from LDS once without holding 64 registers).
-//   Tile j+1 must already be in LDS while tile j is consumed, hence 3 stages;
-//   one barrier per tile.  The steady state is branch-free apart from the
-//   rescale test, so the compiler can interleave the two pipes.
+//   wave owns 32 rows.  K1, K2 and V stream through a 4-stage LDS ring in tiles
+//   of 32 keys.  The kernel needs more than 256 registers per lane, so there is
+//   one wave per SIMD and the overlap of matrix and vector work has to come
+//   from inside the wave.  At d = 64 the vector work of the two softmaxes
+//   (exp2, scale, sums, bf16 packing) costs about as many cycles as the six
+//   matrix products of a tile, so the loop is arranged to keep both pipes busy:
+//   iteration j issues, in one branch-free block,
+//     MFMA  scores of tile j+1 (both maps), P.V of tile j-1 (both maps);
+//     VALU  probabilities of tile j (both maps), row sums;
+//     memory  global loads of tile j+3, LDS stores of tile j+2;
+//   and ends with the masking of tile j+1 (tiles on the causal diagonal and
+//   the ragged last tile only) and the lazy-maximum test of tile j (below),
+//   whose body almost never runs.  Tile j-1's V is read in
+//   iteration j and tile j+1's K too, hence 4 stages; one barrier per tile.
 //
 // Per tile and wave, on MFMA v_mfma_f32_32x32x16_bf16:
 //   S_k^T = K_k Q_k^T          (keys on the M axis, the wave's 32 queries on N),
@@ -33,13 +34,17 @@
 //   once, in the epilogue, followed by the per-head GroupNorm over the dv
 //   channels and the (1 - lambda_init) scale.
 //
-// Online softmax with a lazy maximum: the running maximum m of a row only
-// moves when a new score exceeds it by more than kRescaleLog2 (in log2 units).
-// Until then probabilities are taken against the stale m and may reach
-// 2^kRescaleLog2; the sum l and O share that m, so O / l is unchanged.  The
-// O rescale (the only VALU work proportional to dv) therefore runs only when
-// some row of the wave moves its maximum by that much, which after the first
-// tile is rare.  It multiplies the accumulators where they live, in AGPRs.
+// Online softmax with a lazy maximum: the running maximum m of a row is set
+// exactly from the first tile and afterwards moves only when needed.  Each
+// tile's probabilities are formed against the current, possibly stale, m and
+// may then exceed 1; the sum l and O share that m, so O / l is unchanged.  A
+// lane whose partial sum over the tile (16 of the row's 32 keys) exceeds
+// kSumLimit flags the tile: its exact row maxima are taken, O and l are
+// rescaled, and its probabilities are formed again.  So no probability
+// exceeds kSumLimit, and the O rescale (the only VALU work proportional to dv)
+// and the row maxima (two 16-element reductions per tile) run only when some
+// row's scores climb well past their running maximum, which after the first
+// tile is rare.  The test reuses the row sums the softmax needs anyway.
 //
 // Operand layouts (32x32x16 MFMA; lane l, lh = l / 32, l32 = l % 32):
 //   A operand: row l32, k-slots 8*lh .. 8*lh+7;  B operand: column l32, the same
@@ -61,8 +66,9 @@
 // LDS per stage: K1 and K2 row-major [32][d + 8] (the pad keeps the 16-byte
 // operand reads conflict-free), V row-major [32][dv + 32] (a 64-byte pad puts
 // the 4 rows a half-wave of transposing reads touches in distinct banks).
-// Global loads clamp the key index to the last valid row instead of branching;
-// scores of keys past the end are masked, so the clamped rows contribute 0.
+// Global loads are raw buffer loads whose descriptor ends at the last key of
+// the (batch, head): rows past the end read as zeros without a branch or a
+// clamp, and their scores are masked, so they contribute nothing.
 
 #include "internal.h"
 
@@ -73,6 +79,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -81,16 +88,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kBc = 32;                 // keys per tile
-constexpr float kRescaleLog2 = 8.0f;    // lazy-maximum slack, log2 units
+constexpr float kSumLimit = 4096.0f;    // lazy-maximum bound on a lane's partial tile sum
+constexpr int kBufferDword3 = 0x00020000;  // raw buffer descriptor word 3 for gfx9 parts
 
 template <int D, int DV>
 struct Cfg {
     static constexpr int kBr = kWaves * 32;
-    static constexpr int kStages = 3;
-    static constexpr bool kSplitPV = DV <= 128;  // P.V per map, V operands kept
-    // d <= 64 carries the raw score accumulators across iterations and masks a
-    // working copy; d = 128 (no spare registers) masks in place and copies
-    static constexpr bool kCarryRaw = D <= 64;
+    static constexpr int kStages = 4;
     static constexpr int kKStride = D + 8;
     static constexpr int kVStride = DV + 32;
     static constexpr int kKElems = kBc * kKStride;
@@ -124,9 +128,37 @@ __device__ __forceinline__ float max16(const f32x16& s) {
     return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
 }
 
-// Multiplies every accumulator of o by alpha in place.  The accumulators live
-// in AGPRs; doing the read-multiply-write here keeps the compiler from holding
-// a VGPR copy of all of them around this rarely taken path.
+// Descriptor of `bytes` bytes from `base`; loads at offsets past the end
+// return zeros.  The record count is a 32-bit field, so it is clamped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, kBufferDword3);
+}
+
+// acc += a * b on MFMA with the accumulator held in AGPRs.  Written as inline
+// asm so that this product, alone in the kernel, keeps the AGPR form while
+// the score products (compiler builtins) accumulate in ordinary VGPRs, where
+// the softmax reads them.  The compiler does not see this instruction as an
+// MFMA, so the wait states it would insert are provided by hand: two before
+// the product (a VALU write of an operand register needs them), and
+// mfma_drain before any other instruction touches the accumulators.  Inputs
+// a and b come from LDS reads (ordered by the compiler's s_waitcnt) and from
+// VALU results of the previous tile.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states that let the last mfma_agpr products retire before the
+// accumulators are read or written by other instructions.
+template <int NDB>
+__device__ __forceinline__ void mfma_drain(f32x16 (&o1)[NDB], f32x16 (&o2)[NDB]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o1[db]), "+a"(o2[db]));
+}
+
+// Multiplies every accumulator of o by alpha where it lives, in AGPRs, one
+// register at a time (a plain multiply would stage all of them in VGPRs).
 template <int NDB>
 __device__ __forceinline__ void scale_acc(f32x16 (&o)[NDB], float alpha) {
 #pragma unroll
@@ -146,38 +178,29 @@ __device__ __forceinline__ void scale_acc(f32x16 (&o)[NDB], float alpha) {
     }
 }
 
-// Moves the running maximum of one map when some row needs it (lazy rule).
-template <int NDB>
-__device__ __forceinline__ void maybe_rescale(float mx, float& m, float& l, f32x16 (&o)[NDB]) {
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2)) {
-        const float mrow = fmaxf(mx, xor32(mx));
-        const float mnew = fmaxf(m, mrow);
-        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        l *= alpha;
-        scale_acc<NDB>(o, alpha);
-    }
+// The bf16 probabilities p[e], p[e+1] of a tile packed into pb, added to a
+// row partial sum with one dot product against (1, 1): the sum is taken over
+// the same rounded values that enter P.V.
+__device__ __forceinline__ void pack_pair(bf16x8 (&pb)[2], int e, float pa, float pc, float& sum) {
+    const bf16x2 pr = {(__bf16)pa, (__bf16)pc};
+    u32x4 w = __builtin_bit_cast(u32x4, pb[e >> 3]);
+    w[(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+    pb[e >> 3] = __builtin_bit_cast(bf16x8, w);
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
 }
 
-// Probabilities of one map: p = 2^(s * scale - base), summed into l and
-// packed to bf16 B operands (registers 8kb .. 8kb+7 per 16 keys).
-__device__ __forceinline__ void probabilities(const f32x16& s, float sl2, float base, float& l,
-                                              bf16x8 (&pb)[2]) {
-    float sum0 = 0.f, sum1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kb + e], sl2, -base));
-            if (e & 1)
-                sum1 += p;
-            else
-                sum0 += p;
-            pb[kb][e] = (__bf16)p;
-        }
-    }
-    l += sum0 + sum1;
+// Probabilities p = 2^(s * scale - base) of accumulator registers e, e+1 of a
+// score tile, packed and summed (see pack_pair).
+__device__ __forceinline__ void prob_pair(const f32x16& s, int e, float sl2, float base,
+                                          bf16x8 (&pb)[2], float& sum) {
+    const float pa = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -base));
+    const float pc = __builtin_amdgcn_exp2f(fmaf(s[e + 1], sl2, -base));
+    pack_pair(pb, e, pa, pc, sum);
 }
+
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
 
 template <int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
@@ -225,29 +248,32 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 
     const int nkt_all = (a.Nk + kBc - 1) / kBc;
     const int nkt = CAUSAL ? min(nkt_all, (qt * C::kBr + C::kBr + kBc - 1) / kBc) : nkt_all;
-    const int last_key = a.Nk - 1;
+    // leading tiles in which no row of this wave masks a key
+    const int nfull = CAUSAL ? min(a.Nk / kBc, (wq0 + 1) / kBc) : a.Nk / kBc;
 
     u32x4 rk1[C::kKLoads], rk2[C::kKLoads], rv[C::kVLoads];
 
-    // global -> registers; key indices clamp to the last row (masked later)
+    // global -> registers through descriptors that start at the tile
     auto load_tile = [&](int kt) {
-        const int key0 = kt * kBc;
+        const int64_t key0 = (int64_t)kt * kBc;
+        const int64_t left = (int64_t)a.Nk - key0;
+        const __amdgpu_buffer_rsrc_t r1 = buffer_rsrc(gk1 + key0 * D, left * D * 2);
+        const __amdgpu_buffer_rsrc_t r2 = buffer_rsrc(gk2 + key0 * D, left * D * 2);
+        const __amdgpu_buffer_rsrc_t rvv = buffer_rsrc(gv + key0 * DV, left * DV * 2);
 #pragma unroll
         for (int i = 0; i < C::kKLoads; ++i) {
-            const int c = tid + i * kThreads;
-            const int key = min(key0 + c / (D / 8), last_key);
-            const int ch = c % (D / 8);
-            rk1[i] = *(const u32x4*)(gk1 + (size_t)key * D + ch * 8);
-            rk2[i] = *(const u32x4*)(gk2 + (size_t)key * D + ch * 8);
+            const int off = 16 * (tid + i * kThreads);  // key c / (D/8), channel chunk c % (D/8)
+            rk1[i] = __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, 0);
+            rk2[i] = __builtin_amdgcn_raw_buffer_load_b128(r2, off, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < C::kVLoads; ++i) {
-            const int c = tid + i * kThreads;
-            const int key = min(key0 + c / (DV / 8), last_key);
-            const int ch = c % (DV / 8);
-            rv[i] = *(const u32x4*)(gv + (size_t)key * DV + ch * 8);
+            const int off = 16 * (tid + i * kThreads);
+            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rvv, off, 0, 0);
         }
     };
+
+    auto stage_of = [](int kt) { return kt & (C::kStages - 1); };
 
     auto store_tile = [&](int buf) {
         uint16_t* k1s = smem + buf * C::kStage;
@@ -290,15 +316,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     // keys past the end, and keys after the query under the causal mask, to -inf
     auto mask = [&](int kt, f32x16& s1, f32x16& s2) {
         const int key0 = kt * kBc;
-        const bool need = (CAUSAL && key0 + kBc - 1 > wq0) || (key0 + kBc > a.Nk);
-        if (need) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = key0 + 16 * (r >> 3) + 8 * lh + (r & 7);
-                const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
-                s1[r] = ok ? s1[r] : -INFINITY;
-                s2[r] = ok ? s2[r] : -INFINITY;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 16 * (r >> 3) + 8 * lh + (r & 7);
+            const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
+            s1[r] = ok ? s1[r] : -INFINITY;
+            s2[r] = ok ? s2[r] : -INFINITY;
         }
     };
 
@@ -317,13 +340,39 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     };
 
     const float sl2 = a.scale_log2;
-    float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
+    float m1, m2, l1 = 0.f, l2 = 0.f;
     f32x16 o1[NDB], o2[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         o1[db] = f32x16{};
         o2[db] = f32x16{};
     }
+
+    // P.V of one tile for both maps (the last tile; inside the loop the same
+    // products are spread over the issue slots)
+    auto pv = [&](int buf, const bf16x8 (&p1)[2], const bf16x8 (&p2)[2]) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 va = v_operand(buf, db, kb);
+                mfma_agpr(o1[db], va, p1[kb]);
+                mfma_agpr(o2[db], va, p2[kb]);
+            }
+        }
+    };
+
+    // Per-tile state, two copies used alternately (tile j in X[j % 2]): the
+    // masked scores of the tile and, once formed, its probabilities.  In
+    // iteration j the other copy still holds tile j-1's probabilities (read by
+    // its P.V) and receives tile j+1's scores, so nothing is copied between
+    // iterations and the new probabilities never have to wait for the
+    // previous tile's products to be issued.
+    struct TileState {
+        f32x16 s1, s2;
+        bf16x8 p1[2], p2[2];
+    };
+    TileState A, B;
 
     // prologue: tiles 0 and 1 into LDS, tile 2 into registers, scores of tile 0
     load_tile(0);
@@ -332,82 +381,186 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     store_tile(1);
     __syncthreads();
     load_tile(2);
-    // n1, n2: score accumulators of the next tile; s1, s2: tile j's scores
-    f32x16 n1, n2, s1, s2;
-    if constexpr (C::kCarryRaw) {
-        scores(0, n1, n2);
-    } else {
-        scores(0, s1, s2);
-        mask(0, s1, s2);
+    scores(0, A.s1, A.s2);
+    if (nfull < 1) mask(0, A.s1, A.s2);
+    {
+        // exact row maxima of tile 0 start the running maxima
+        const float x1 = max16(A.s1) * sl2, x2 = max16(A.s2) * sl2;
+        m1 = fmaxf(x1, xor32(x1));
+        m2 = fmaxf(x2, xor32(x2));
     }
 
-    int bj = 0;  // stage of tile j; tile j+1 is in (bj+1)%3, tile j+2 goes to (bj+2)%3
-    for (int j = 0; j < nkt; ++j) {
-        const int bn = bj == 2 ? 0 : bj + 1;
-        const int bw = bn == 2 ? 0 : bn + 1;
+    // Issue plan of one iteration.  The body is a fixed sequence of kSlots
+    // slots, each holding one MFMA and a planned share of the vector work,
+    // fenced by scheduling barriers, so that the compiler cannot bunch the
+    // matrix products together and leave the softmax to run after them (it
+    // otherwise does, and both pipes then idle half of the time):
+    //   slots 0 .. kScore-1     score products of tile j+1, each K operand
+    //                           read kKAhead products ahead;
+    //   slots kScore ..         P.V products of tile j-1, each V operand read
+    //                           kLookahead operand pairs ahead;
+    //   vector work             the 16 probability pairs of tile j spread
+    //                           over the slots (starting in a slot -1 that
+    //                           has no product and covers the first K read),
+    //                           the LDS store of tile j+2 and the global loads
+    //                           of tile j+3 early.
+    constexpr int kScore = 2 * NKB;
+    constexpr int kPairsV = 2 * NDB;           // V operands (db, kb)
+    constexpr int kSlots = kScore + 2 * kPairsV;
+    constexpr int kLookahead = 3;              // V operands read ahead
+    constexpr int kKAhead = 4;                 // K operands read ahead
+    constexpr int kStoreSlot = 1, kLoadSlot = 2;
+    // probability pair k (map k / 8, registers 2 (k % 8) and +1) starts in slot
+    auto pair_slot = [](int k) { return k * (kSlots - 3) / 16 - 1; };
+    static_assert(15 * (kSlots - 3) / 16 - 1 + 2 < kSlots, "pairs must finish in the slots");
 
-        if constexpr (C::kCarryRaw) {
-            s1 = n1;
-            s2 = n2;
-            mask(j, s1, s2);
-        }
-
-        // step 0: row maxima of tile j and the rare rescale
-        maybe_rescale<NDB>(max16(s1) * sl2, m1, l1, o1);
-        maybe_rescale<NDB>(max16(s2) * sl2, m2, l2, o2);
+    // One iteration j (see the header); cur holds tile j, oth tile j-1 and
+    // then j+1.  PREV: tile j-1 exists; NEXT: tile j+1 exists.
+    auto iteration = [&](auto prev, auto next, int j, TileState& cur, TileState& oth) {
+        constexpr bool PREV = decltype(prev)::value;
+        constexpr bool NEXT = decltype(next)::value;
         const float base1 = m1 == -INFINITY ? 0.f : m1;
         const float base2 = m2 == -INFINITY ? 0.f : m2;
 
-        // step 1: scores of tile j+1 on MFMA while the VALU turns tile j into P
-        scores(bn, n1, n2);
-        bf16x8 p1[2], p2[2];
-        probabilities(s1, sl2, base1, l1, p1);
+        bf16x8 ka[kScore], va[kPairsV];
+        const uint16_t* k1s = smem + stage_of(j + 1) * C::kStage + krow * C::kKStride + 8 * lh;
+        // K operand i: map i % 2, channels 16 (i / 2) + 8 lh ..
+        auto read_k = [&](int i) {
+            ka[i] = *(const bf16x8*)(k1s + (i & 1) * C::kKElems + 16 * (i >> 1));
+        };
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int i = 0; i < kKAhead; ++i) read_k(i);
+        }
+        const int vbuf = stage_of(j - 1);
+        if constexpr (PREV) {
+#pragma unroll
+            for (int q = 0; q < kLookahead; ++q) va[q] = v_operand(vbuf, q >> 1, q & 1);
+        }
+        float t1a = 0.f, t1b = 0.f, t2a = 0.f, t2b = 0.f;
+        float xs[32];  // probabilities in flight, element 16 map + register
+        __builtin_amdgcn_sched_barrier(0);
 
-        if constexpr (C::kSplitPV) {
-            // step 2: P.V for map 1 while map 2's probabilities are formed
-            bf16x8 va[NDB][2];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    va[db][kb] = v_operand(bj, db, kb);
-                    o1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb], p1[kb], o1[db], 0, 0, 0);
+        for (int slot = -1; slot < kSlots; ++slot) {
+            if (slot < 0) {
+                // no product: the first K operands are still on their way
+            } else if (slot < kScore) {
+                if constexpr (NEXT) {
+                    const int kb = slot >> 1;
+                    if (slot + kKAhead < kScore) read_k(slot + kKAhead);
+                    if ((slot & 1) == 0)
+                        oth.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            ka[slot], qf1[kb], kb == 0 ? f32x16{} : oth.s1, 0, 0, 0);
+                    else
+                        oth.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            ka[slot], qf2[kb], kb == 0 ? f32x16{} : oth.s2, 0, 0, 0);
+                }
+            } else {
+                if constexpr (PREV) {
+                    const int i = slot - kScore, q = i >> 1;
+                    if ((i & 1) == 0) {
+                        if (q + kLookahead < kPairsV)
+                            va[q + kLookahead] = v_operand(vbuf, (q + kLookahead) >> 1, (q + kLookahead) & 1);
+                        mfma_agpr(o1[q >> 1], va[q], oth.p1[q & 1]);
+                    } else {
+                        mfma_agpr(o2[q >> 1], va[q], oth.p2[q & 1]);
+                    }
                 }
             }
-            probabilities(s2, sl2, base2, l2, p2);
-            // step 3: P.V for map 2 while the tile traffic goes on
+            // probability pair k: scale at pair_slot(k), exp2 one slot later,
+            // sums and bf16 packing one slot after that, so that the work of
+            // a slot is independent and no chain latency stalls the wave
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    o2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][kb], p2[kb], o2[db], 0, 0, 0);
-            }
-        } else {
-            probabilities(s2, sl2, base2, l2, p2);
-            // step 2: P.V for both maps, each V operand read once
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 va = v_operand(bj, db, kb);
-                    o1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1[kb], o1[db], 0, 0, 0);
-                    o2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2[kb], o2[db], 0, 0, 0);
+            for (int k = 0; k < 16; ++k) {
+                const int e = 2 * (k & 7);
+                const f32x16& sk = k < 8 ? cur.s1 : cur.s2;
+                const float bk = k < 8 ? base1 : base2;
+                if (pair_slot(k) == slot) {
+                    xs[2 * k] = fmaf(sk[e], sl2, -bk);
+                    xs[2 * k + 1] = fmaf(sk[e + 1], sl2, -bk);
                 }
+                if (pair_slot(k) + 1 == slot) {
+                    xs[2 * k] = __builtin_amdgcn_exp2f(xs[2 * k]);
+                    xs[2 * k + 1] = __builtin_amdgcn_exp2f(xs[2 * k + 1]);
+                }
+                if (pair_slot(k) + 2 == slot) {
+                    if (k < 8)
+                        pack_pair(cur.p1, e, xs[2 * k], xs[2 * k + 1], (k & 1) ? t1b : t1a);
+                    else
+                        pack_pair(cur.p2, e, xs[2 * k], xs[2 * k + 1], (k & 1) ? t2b : t2a);
+                }
+            }
+            if (slot == kStoreSlot) store_tile(stage_of(j + 2));  // zeros once past the end
+            if (slot == kLoadSlot) load_tile(j + 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Keep the common-path probabilities ahead of the rare branch below
+        // (which forms them again) rather than sunk into its other side.
+        asm volatile("" ::"v"(cur.p1[0]), "v"(cur.p1[1]), "v"(cur.p2[0]), "v"(cur.p2[1]),
+                     "v"(t1a), "v"(t1b), "v"(t2a), "v"(t2b));
+
+        // causal diagonal or ragged last tile: mask tile j+1 before its
+        // probabilities are formed in the next iteration
+        if constexpr (NEXT) {
+            if (j + 1 >= nfull) mask(j + 1, oth.s1, oth.s2);
+        }
+        // lazy-maximum test on tile j: a large partial sum means that some
+        // scores passed the stale maximum; take the exact maxima of the tile,
+        // rescale, and form its probabilities again
+        float t1 = t1a + t1b, t2 = t2a + t2b;
+        if (__builtin_amdgcn_ballot_w64(t1 > kSumLimit || t2 > kSumLimit)) {
+            const float x1 = max16(cur.s1) * sl2, x2 = max16(cur.s2) * sl2;
+            const float mn1 = fmaxf(m1, fmaxf(x1, xor32(x1)));
+            const float mn2 = fmaxf(m2, fmaxf(x2, xor32(x2)));
+            const float al1 = mn1 == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m1 - mn1);
+            const float al2 = mn2 == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mn2);
+            m1 = mn1;
+            m2 = mn2;
+            l1 *= al1;
+            l2 *= al2;
+            mfma_drain<NDB>(o1, o2);
+            scale_acc<NDB>(o1, al1);
+            scale_acc<NDB>(o2, al2);
+            const float nb1 = m1 == -INFINITY ? 0.f : m1;
+            const float nb2 = m2 == -INFINITY ? 0.f : m2;
+            t1 = t2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                prob_pair(cur.s1, e, sl2, nb1, cur.p1, t1);
+                prob_pair(cur.s2, e, sl2, nb2, cur.p2, t2);
             }
         }
-
-        store_tile(bw);      // tile j+2 (stale and unused once past the end)
-        load_tile(j + 3);    // clamped rows once past the end
-        if constexpr (!C::kCarryRaw) mask(j + 1, n1, n2);
+        l1 += t1;
+        l2 += t2;
         __syncthreads();
-        if constexpr (!C::kCarryRaw) {
-            s1 = n1;
-            s2 = n2;
+    };
+
+    const bool_c<true> T;
+    const bool_c<false> F;
+    if (nkt == 1) {
+        iteration(F, F, 0, A, B);
+        pv(stage_of(0), A.p1, A.p2);
+    } else {
+        iteration(F, T, 0, A, B);
+        // tile j lives in A for even j and in B for odd j
+        int j = 1;
+        for (; j + 1 < nkt - 1; j += 2) {
+            iteration(T, T, j, B, A);
+            iteration(T, T, j + 1, A, B);
         }
-        bj = bn;
+        if (j < nkt - 1) {
+            iteration(T, T, j, B, A);
+            iteration(T, F, j + 1, A, B);
+            pv(stage_of(j + 1), A.p1, A.p2);
+        } else {
+            iteration(T, F, j, B, A);
+            pv(stage_of(j), B.p1, B.p2);
+        }
     }
 
     // epilogue: D = O1/l1 - lambda O2/l2, then GroupNorm over the dv channels
+    mfma_drain<NDB>(o1, o2);
     const float lam = a.lam[h];
     const float L1 = l1 + xor32(l1);
     const float L2 = l2 + xor32(l2);
@@ -477,7 +630,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
                                hipStream_t stream) {
     if (d == 32 && dv == 64) return launch_dims<32, 64>(a, causal, stream);
     if (d == 64 && dv == 128) return launch_dims<64, 128>(a, causal, stream);
-    if (d == 128 && dv == 256) return launch_dims<128, 256>(a, causal, stream);
+    if (d == 128 && dv == 256) return launch_prefill_bf16_wide(a, d, dv, causal, stream);
     return hipErrorInvalidValue;
 }
 
