@@ -8,30 +8,35 @@
 // one memory pass ("Throughput and Hardware Realities"); this is that kernel.
 //
 // Work decomposition
-//   One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
-//   wave owns 32 rows.  K1, K2 and V stream through a 4-stage LDS ring in tiles
-//   of 32 keys.  The kernel needs more than 256 registers per lane, so there is
-//   one wave per SIMD and the overlap of matrix and vector work has to come
-//   from inside the wave.  At d = 64 the vector work of the two softmaxes
-//   (exp2, scale, sums, bf16 packing) costs about as many cycles as the six
-//   matrix products of a tile, so the loop is arranged to keep both pipes busy:
-//   iteration j issues, in one branch-free block,
-//     MFMA  scores of tile j+1 (both maps), P.V of tile j-1 (both maps);
-//     VALU  probabilities of tile j (both maps), row sums;
-//     memory  global loads of tile j+3, LDS stores of tile j+2;
+//   One workgroup = 8 wavefronts = 128 query rows of one (batch, head).  Wave
+//   w owns query block w % 4 (32 rows) of map w / 4: the two softmax maps of
+//   a row are computed by two waves, and the lambda-weighted subtraction is
+//   done once, through LDS, in the epilogue.  Splitting by map halves the
+//   registers of a wave (one O^T accumulator, one score tile), which lets two
+//   waves share each SIMD; a wave waiting on LDS or on the barrier then
+//   leaves the SIMD to the other.  Waves w and w + 4 run on the same SIMD, one
+//   per map.  K1, K2 and V stream through a 4-stage LDS ring in tiles of 32
+//   keys; each wave reads the K tile of its own map and the shared V tile.
+//
+//   Iteration j of a wave issues, in one branch-free block,
+//     MFMA  scores of tile j+1, P.V of tile j-1;
+//     VALU  probabilities of tile j, row sums;
+//     memory  global loads of tile j+3, LDS stores of tile j+2 (all waves);
 //   and ends with the masking of tile j+1 (tiles on the causal diagonal and
 //   the ragged last tile only) and the lazy-maximum test of tile j (below),
-//   whose body almost never runs.  Tile j-1's V is read in
-//   iteration j and tile j+1's K too, hence 4 stages; one barrier per tile.
+//   whose body almost never runs.  Tile j-1's V is read in iteration j and
+//   tile j+1's K too, hence 4 stages; one barrier per tile.  The block is a
+//   fixed sequence of slots, one MFMA each with a planned share of the vector
+//   work, fenced by scheduling barriers so that the compiler cannot bunch the
+//   products together.
 //
-// Per tile and wave, on MFMA v_mfma_f32_32x32x16_bf16:
+// Per tile and wave, on MFMA v_mfma_f32_32x32x16_bf16 (k = the wave's map):
 //   S_k^T = K_k Q_k^T          (keys on the M axis, the wave's 32 queries on N),
-//   O_k^T = alpha_k O_k^T + V^T P_k^T   for k = 1, 2.
+//   O_k^T = alpha O_k^T + V^T P_k^T.
 //   With the transposed score tile every query lives in one lane pair (lanes
 //   l and l+32), so online-softmax row statistics are in-lane reductions plus
-//   one exchange, and the rescale of O^T is a per-lane scalar.  The two maps
-//   keep separate (max, sum, O) states; the lambda-weighted subtraction happens
-//   once, in the epilogue, followed by the per-head GroupNorm over the dv
+//   one exchange, and the rescale of O^T is a per-lane scalar.  The epilogue
+//   forms D = O_1 / l_1 - lambda O_2 / l_2, the per-head GroupNorm over the dv
 //   channels and the (1 - lambda_init) scale.
 //
 // Online softmax with a lazy maximum: the running maximum m of a row is set
@@ -42,9 +47,9 @@
 // kSumLimit flags the tile: its exact row maxima are taken, O and l are
 // rescaled, and its probabilities are formed again.  So no probability
 // exceeds kSumLimit, and the O rescale (the only VALU work proportional to dv)
-// and the row maxima (two 16-element reductions per tile) run only when some
-// row's scores climb well past their running maximum, which after the first
-// tile is rare.  The test reuses the row sums the softmax needs anyway.
+// and the row maxima run only when some row's scores climb well past their
+// running maximum, which after the first tile is rare.  The test reuses the
+// row sums the softmax needs anyway.
 //
 // Operand layouts (32x32x16 MFMA; lane l, lh = l / 32, l32 = l % 32):
 //   A operand: row l32, k-slots 8*lh .. 8*lh+7;  B operand: column l32, the same
@@ -74,6 +79,10 @@
 
 #include <math.h>
 
+// The direct-to-LDS loads set M0 in inline asm; nothing else in this file
+// uses M0, so the reserved-register clobber is safe here.
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace diffattn {
 namespace {
 
@@ -83,27 +92,36 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kBlocks = 4;              // query blocks of 32 rows per workgroup
 constexpr int kBc = 32;                 // keys per tile
 constexpr float kSumLimit = 4096.0f;    // lazy-maximum bound on a lane's partial tile sum
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer descriptor word 3 for gfx9 parts
 
 template <int D, int DV>
 struct Cfg {
-    static constexpr int kBr = kWaves * 32;
-    static constexpr int kStages = 4;
-    static constexpr int kKStride = D + 8;
-    static constexpr int kVStride = DV + 32;
-    static constexpr int kKElems = kBc * kKStride;
-    static constexpr int kVElems = kBc * kVStride;
+    static constexpr int kBr = kBlocks * 32;
+    static constexpr int kStages = 8;                      // LDS ring (a power of two)
+    static constexpr int kAhead = 6;                       // tiles loaded ahead of use
+    static constexpr int kKElems = kBc * D;
+    static constexpr int kVElems = kBc * DV;
     static constexpr int kStage = 2 * kKElems + kVElems;  // bf16 elements per stage
     static constexpr int kKChunks = kBc * D / 8;           // 16-byte chunks per K tile
     static constexpr int kVChunks = kBc * DV / 8;
-    static constexpr int kKLoads = (kKChunks + kThreads - 1) / kThreads;
-    static constexpr int kVLoads = (kVChunks + kThreads - 1) / kThreads;
+    static constexpr int kChunks = 2 * kKChunks + kVChunks;
+    static constexpr int kLoads = kChunks / kThreads;      // load instructions per wave and tile
+    static_assert(kChunks % kThreads == 0, "tile must split evenly over the threads");
+    static_assert(kKChunks % 64 == 0, "K regions must start on a wave boundary");
+    // a stage is refilled kStages - kAhead tiles after the barrier that ends
+    // its last reads (V of tile t is read in iteration t + 1)
+    static_assert(kAhead + 2 <= kStages, "ring too small for the load distance");
+    // epilogue exchange: one float per (query block, accumulator, lane)
+    static constexpr int kXchgFloats = kBlocks * (DV / 32) * 16 * 64;
+    static constexpr int kSmemElems =
+        kStages * kStage > 2 * kXchgFloats ? kStages * kStage : 2 * kXchgFloats;
 };
 
 __device__ __forceinline__ int swap23(int r) {
@@ -112,11 +130,32 @@ __device__ __forceinline__ int swap23(int r) {
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// LDS tiles are stored without padding; 16-byte chunk ch of row r sits at
+// chunk position ch ^ swz(r) of its row, which spreads the rows an MFMA
+// operand read touches at once over distinct banks.  K operand reads take
+// rows {0,1,2,3,8,9,10,11} (+4, +16, ...) at one chunk column per 8 lanes;
+// transposing V reads take 4 consecutive rows at one 32-byte column per 16
+// lanes.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+    if constexpr (D == 64)
+        return (r & 3) | ((r >> 1) & 4);        // 8 chunks per row
+    else
+        return ((r >> 1) & 1) | ((r >> 2) & 2);  // 4 chunks per row (two rows per 128 B)
+}
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+
 // a*b - c*d with both products rounded before the subtraction (no fused
 // multiply-add), so equal operands cancel to exactly zero
 __device__ __forceinline__ float diff_of_products(float a, float b, float c, float d) {
 #pragma clang fp contract(off)
     return a * b - c * d;
+}
+
+// a*b rounded on its own (the second product of diff_of_products)
+__device__ __forceinline__ float product(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
 }
 
 __device__ __forceinline__ float max16(const f32x16& s) {
@@ -128,54 +167,19 @@ __device__ __forceinline__ float max16(const f32x16& s) {
     return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
 }
 
-// Descriptor of `bytes` bytes from `base`; loads at offsets past the end
-// return zeros.  The record count is a 32-bit field, so it is clamped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+// Raw buffer descriptor of `bytes` bytes from `base` (wave-uniform values),
+// as four SGPRs: base address (48 bits, stride 0), record count in bytes,
+// word 3.  Loads at offsets past the end return zeros.  The record count is
+// a 32-bit field, so it is clamped.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, kBufferDword3);
-}
-
-// acc += a * b on MFMA with the accumulator held in AGPRs.  Written as inline
-// asm so that this product, alone in the kernel, keeps the AGPR form while
-// the score products (compiler builtins) accumulate in ordinary VGPRs, where
-// the softmax reads them.  The compiler does not see this instruction as an
-// MFMA, so the wait states it would insert are provided by hand: two before
-// the product (a VALU write of an operand register needs them), and
-// mfma_drain before any other instruction touches the accumulators.  Inputs
-// a and b come from LDS reads (ordered by the compiler's s_waitcnt) and from
-// VALU results of the previous tile.
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Wait states that let the last mfma_agpr products retire before the
-// accumulators are read or written by other instructions.
-template <int NDB>
-__device__ __forceinline__ void mfma_drain(f32x16 (&o1)[NDB], f32x16 (&o2)[NDB]) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o1[db]), "+a"(o2[db]));
-}
-
-// Multiplies every accumulator of o by alpha where it lives, in AGPRs, one
-// register at a time (a plain multiply would stage all of them in VGPRs).
-template <int NDB>
-__device__ __forceinline__ void scale_acc(f32x16 (&o)[NDB], float alpha) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = o[db][r];
-            float tmp;
-            asm volatile(
-                "v_accvgpr_read_b32 %1, %0\n\t"
-                "v_mul_f32 %1, %1, %2\n\t"
-                "v_accvgpr_write_b32 %0, %1"
-                : "+a"(x), "=&v"(tmp)
-                : "v"(alpha));
-            o[db][r] = x;
-        }
-    }
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffff));
+    r[2] = __builtin_amdgcn_readfirstlane((int)n);
+    r[3] = kBufferDword3;
+    return r;
 }
 
 // The bf16 probabilities p[e], p[e+1] of a tile packed into pb, added to a
@@ -207,13 +211,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     using C = Cfg<D, DV>;
     constexpr int NDB = DV / 32;
     constexpr int NKB = D / 16;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[C::kStages * C::kStage];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::kSmemElems];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int lh = lane >> 5;
+    const int qb = wave & (kBlocks - 1);  // query block
+    const int map = wave >> 2;            // 0: first softmax map, 1: the lambda map
 
     // longest causal tiles first: the first B*H blocks take the last query tile
     const int BH = a.B * a.H;
@@ -223,142 +229,142 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     const int qt = CAUSAL ? (nqt - 1 - t) : t;
     const int h = bh % a.H;
 
-    const uint16_t* gq1 = (const uint16_t*)a.q1 + (size_t)bh * a.Nq * D;
-    const uint16_t* gq2 = (const uint16_t*)a.q2 + (size_t)bh * a.Nq * D;
+    const uint16_t* gq = (const uint16_t*)(map ? a.q2 : a.q1) + (size_t)bh * a.Nq * D;
     const uint16_t* gk1 = (const uint16_t*)a.k1 + (size_t)bh * a.Nk * D;
     const uint16_t* gk2 = (const uint16_t*)a.k2 + (size_t)bh * a.Nk * D;
     const uint16_t* gv = (const uint16_t*)a.v + (size_t)bh * a.Nk * DV;
     __bf16* gout = (__bf16*)a.out + (size_t)bh * a.Nq * DV;
 
-    const int wq0 = qt * C::kBr + wave * 32;  // first query row of this wave
-    const int qrow = wq0 + l32;               // this lane's query row
+    const int wq0 = qt * C::kBr + qb * 32;  // first query row of this wave
+    const int qrow = wq0 + l32;             // this lane's query row
 
-    // Q fragments as B operands: column = query, k-slots = channels 16kb + 8lh ..
-    bf16x8 qf1[NKB], qf2[NKB];
+    // Q fragments of the wave's map as B operands: column = query,
+    // k-slots = channels 16kb + 8lh ..
+    bf16x8 qf[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        if (qrow < a.Nq) {
-            qf1[kb] = *(const bf16x8*)(gq1 + (size_t)qrow * D + 16 * kb + 8 * lh);
-            qf2[kb] = *(const bf16x8*)(gq2 + (size_t)qrow * D + 16 * kb + 8 * lh);
-        } else {
-            qf1[kb] = bf16x8{};
-            qf2[kb] = bf16x8{};
-        }
-    }
+    for (int kb = 0; kb < NKB; ++kb)
+        qf[kb] = qrow < a.Nq ? *(const bf16x8*)(gq + (size_t)qrow * D + 16 * kb + 8 * lh)
+                             : bf16x8{};
 
     const int nkt_all = (a.Nk + kBc - 1) / kBc;
     const int nkt = CAUSAL ? min(nkt_all, (qt * C::kBr + C::kBr + kBc - 1) / kBc) : nkt_all;
     // leading tiles in which no row of this wave masks a key
     const int nfull = CAUSAL ? min(a.Nk / kBc, (wq0 + 1) / kBc) : a.Nk / kBc;
 
-    u32x4 rk1[C::kKLoads], rk2[C::kKLoads], rv[C::kVLoads];
-
-    // global -> registers through descriptors that start at the tile
-    auto load_tile = [&](int kt) {
+    // Tile loads go from global memory straight into the LDS ring
+    // (buffer_load_dwordx4 ... lds: lane i of an instruction writes its 16
+    // bytes at M0 + 16 i).  The tile's chunk positions, K1 then K2 then V, form
+    // kChunks / 64 instructions; wave w issues instructions w, w + 8, ...  Each
+    // lane loads the global chunk that belongs at its position under the
+    // swizzle.  Regions start on instruction boundaries, so an instruction
+    // reads one tensor; its descriptor ends at the last key, and lanes past
+    // it write zeros.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // provably uniform copy
+    int ld_off[C::kLoads];  // per instruction: this lane's byte offset in the tile
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+        const int c0 = 64 * (wave_u + i * (kThreads / 64));
+        if (c0 < 2 * C::kKChunks) {
+            const int pos = (c0 < C::kKChunks ? c0 : c0 - C::kKChunks) + lane;
+            const int row = pos / (D / 8);
+            ld_off[i] = row * D * 2 + 16 * ((pos % (D / 8)) ^ k_swz<D>(row));
+        } else {
+            const int pos = c0 - 2 * C::kKChunks + lane;
+            const int row = pos / (DV / 8);
+            ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz(row));
+        }
+    }
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;  // LDS byte address
+    auto stage_of = [](int kt) { return kt & (C::kStages - 1); };
+    auto issue_tile = [&](int kt) {
         const int64_t key0 = (int64_t)kt * kBc;
         const int64_t left = (int64_t)a.Nk - key0;
-        const __amdgpu_buffer_rsrc_t r1 = buffer_rsrc(gk1 + key0 * D, left * D * 2);
-        const __amdgpu_buffer_rsrc_t r2 = buffer_rsrc(gk2 + key0 * D, left * D * 2);
-        const __amdgpu_buffer_rsrc_t rvv = buffer_rsrc(gv + key0 * DV, left * DV * 2);
+        const uint32_t stage = smem_base + 2u * (uint32_t)(stage_of(kt) * C::kStage);
 #pragma unroll
-        for (int i = 0; i < C::kKLoads; ++i) {
-            const int off = 16 * (tid + i * kThreads);  // key c / (D/8), channel chunk c % (D/8)
-            rk1[i] = __builtin_amdgcn_raw_buffer_load_b128(r1, off, 0, 0);
-            rk2[i] = __builtin_amdgcn_raw_buffer_load_b128(r2, off, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < C::kVLoads; ++i) {
-            const int off = 16 * (tid + i * kThreads);
-            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rvv, off, 0, 0);
+        for (int i = 0; i < C::kLoads; ++i) {
+            const int c0 = 64 * (wave_u + i * (kThreads / 64));
+            const bool in_k = c0 < 2 * C::kKChunks;
+            const uint16_t* base = in_k ? (c0 < C::kKChunks ? gk1 : gk2) + key0 * D : gv + key0 * DV;
+            const i32x4 rsrc = sgpr_rsrc(base, left * (in_k ? D : DV) * 2);
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + 16u * (uint32_t)c0);
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(m0), "v"(ld_off[i]), "s"(rsrc)
+                         : "memory", "m0");
         }
     };
-
-    auto stage_of = [](int kt) { return kt & (C::kStages - 1); };
-
-    auto store_tile = [&](int buf) {
-        uint16_t* k1s = smem + buf * C::kStage;
-        uint16_t* k2s = k1s + C::kKElems;
-        uint16_t* vs = k2s + C::kKElems;
-#pragma unroll
-        for (int i = 0; i < C::kKLoads; ++i) {
-            const int c = tid + i * kThreads;
-            if (C::kKChunks % kThreads == 0 || c < C::kKChunks) {
-                const int row = c / (D / 8), ch = c % (D / 8);
-                *(u32x4*)(k1s + row * C::kKStride + ch * 8) = rk1[i];
-                *(u32x4*)(k2s + row * C::kKStride + ch * 8) = rk2[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < C::kVLoads; ++i) {
-            const int c = tid + i * kThreads;
-            if (C::kVChunks % kThreads == 0 || c < C::kVChunks) {
-                const int row = c / (DV / 8), ch = c % (DV / 8);
-                *(u32x4*)(vs + row * C::kVStride + ch * 8) = rv[i];
-            }
-        }
+    // The loads above are invisible to the compiler's counters: before the
+    // barrier that publishes tile t, each wave waits until at most N of its
+    // own loads are still in flight (loads complete in order).
+    auto wait_loads = [](auto n) {
+        constexpr int N = decltype(n)::value;
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
     };
 
     const int krow = swap23(l32);
-    auto scores = [&](int buf, f32x16& s1, f32x16& s2) {
-        const uint16_t* k1s = smem + buf * C::kStage;
-        const uint16_t* k2s = k1s + C::kKElems;
-        s1 = f32x16{};
-        s2 = f32x16{};
+    // this lane's pieces of the wave's K tile (A operand): row krow, chunk
+    // 2 kb + lh under the swizzle, in bf16 elements from the stage start
+    int k_off[NKB];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const bf16x8 ka1 = *(const bf16x8*)(k1s + krow * C::kKStride + 16 * kb + 8 * lh);
-            const bf16x8 ka2 = *(const bf16x8*)(k2s + krow * C::kKStride + 16 * kb + 8 * lh);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf1[kb], s1, 0, 0, 0);
-            s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2, qf2[kb], s2, 0, 0, 0);
-        }
+    for (int kb = 0; kb < NKB; ++kb)
+        k_off[kb] = map * C::kKElems + krow * D + 8 * ((2 * kb + lh) ^ k_swz<D>(krow));
+    auto k_operand = [&](int buf, int kb) {
+        return *(const bf16x8*)(smem + buf * C::kStage + k_off[kb]);
+    };
+    auto scores = [&](int buf, f32x16& s) {
+        s = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(buf, kb), qf[kb], s, 0, 0, 0);
     };
 
     // keys past the end, and keys after the query under the causal mask, to -inf
-    auto mask = [&](int kt, f32x16& s1, f32x16& s2) {
+    auto mask = [&](int kt, f32x16& s) {
         const int key0 = kt * kBc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = key0 + 16 * (r >> 3) + 8 * lh + (r & 7);
             const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
-            s1[r] = ok ? s1[r] : -INFINITY;
-            s2[r] = ok ? s2[r] : -INFINITY;
+            s[r] = ok ? s[r] : -INFINITY;
         }
     };
 
-    // per-lane pieces of the transposing V read: key e of 4, channel offset 4r
+    // per-lane pieces of the transposing V read: row e of 4 (e = (lane%16)/4,
+    // plus 8 for the upper half-wave), channels 32 db + 16 (vg%2) + 4 (lane%4);
+    // under the swizzle the chunk of channel group (db, vg%2) moves to
+    // (4 db + c0) ^ 2e with c0 = 2 (vg%2) + (lane%4)/2, which is
+    // ((c0 ^ 2e) ^ 4 (db%2)) + 8 (db/2).
     const int vg = lane >> 4;
-    const int v_lane_off = (8 * (vg >> 1) + ((lane & 15) >> 2)) * C::kVStride +
-                           16 * (vg & 1) + 4 * (lane & 3);
+    const int ve = (lane & 15) >> 2;
+    const int vw = (2 * (vg & 1) + ((lane & 3) >> 1)) ^ (2 * ve);
+    const int v_lane_row = 2 * C::kKElems + (8 * (vg >> 1) + ve) * DV + 4 * (lane & 1);
+    const int v_off_even = v_lane_row + 8 * vw;
+    const int v_off_odd = v_lane_row + 8 * (vw ^ 4);
     auto v_operand = [&](int buf, int db, int kb) {
-        const uint16_t* vp = smem + buf * C::kStage + 2 * C::kKElems + v_lane_off +
-                             16 * kb * C::kVStride + 32 * db;
+        const uint16_t* vp = smem + buf * C::kStage + ((db & 1) ? v_off_odd : v_off_even) +
+                             64 * (db >> 1) + 16 * kb * DV;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)vp);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(vp + 4 * C::kVStride));
+            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(vp + 4 * DV));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
     const float sl2 = a.scale_log2;
-    float m1, m2, l1 = 0.f, l2 = 0.f;
-    f32x16 o1[NDB], o2[NDB];
+    float m, l = 0.f;
+    f32x16 o[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        o1[db] = f32x16{};
-        o2[db] = f32x16{};
-    }
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
 
-    // P.V of one tile for both maps (the last tile; inside the loop the same
-    // products are spread over the issue slots)
-    auto pv = [&](int buf, const bf16x8 (&p1)[2], const bf16x8 (&p2)[2]) {
+    // P.V of one tile (the last tile; inside the loop the same products are
+    // spread over the issue slots)
+    auto pv = [&](int buf, const bf16x8 (&p)[2]) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 va = v_operand(buf, db, kb);
-                mfma_agpr(o1[db], va, p1[kb]);
-                mfma_agpr(o2[db], va, p2[kb]);
-            }
+            for (int kb = 0; kb < 2; ++kb)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(buf, db, kb), p[kb], o[db],
+                                                                0, 0, 0);
         }
     };
 
@@ -369,170 +375,129 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     // iterations and the new probabilities never have to wait for the
     // previous tile's products to be issued.
     struct TileState {
-        f32x16 s1, s2;
-        bf16x8 p1[2], p2[2];
+        f32x16 s;
+        bf16x8 p[2];
     };
     TileState A, B;
 
-    // prologue: tiles 0 and 1 into LDS, tile 2 into registers, scores of tile 0
-    load_tile(0);
-    store_tile(0);
-    load_tile(1);
-    store_tile(1);
+    // prologue: tiles 0 .. kAhead-1 in flight; tiles 0 and 1 complete
+#pragma unroll
+    for (int t0 = 0; t0 < C::kAhead; ++t0) issue_tile(t0);
+    wait_loads(std::integral_constant<int, (C::kAhead - 2) * C::kLoads>{});
     __syncthreads();
-    load_tile(2);
-    scores(0, A.s1, A.s2);
-    if (nfull < 1) mask(0, A.s1, A.s2);
+    scores(0, A.s);
+    if (nfull < 1) mask(0, A.s);
     {
         // exact row maxima of tile 0 start the running maxima
-        const float x1 = max16(A.s1) * sl2, x2 = max16(A.s2) * sl2;
-        m1 = fmaxf(x1, xor32(x1));
-        m2 = fmaxf(x2, xor32(x2));
+        const float x = max16(A.s) * sl2;
+        m = fmaxf(x, xor32(x));
     }
 
-    // Issue plan of one iteration.  The body is a fixed sequence of kSlots
-    // slots, each holding one MFMA and a planned share of the vector work,
-    // fenced by scheduling barriers, so that the compiler cannot bunch the
-    // matrix products together and leave the softmax to run after them (it
-    // otherwise does, and both pipes then idle half of the time):
-    //   slots 0 .. kScore-1     score products of tile j+1, each K operand
-    //                           read kKAhead products ahead;
-    //   slots kScore ..         P.V products of tile j-1, each V operand read
-    //                           kLookahead operand pairs ahead;
-    //   vector work             the 16 probability pairs of tile j spread
-    //                           over the slots (starting in a slot -1 that
-    //                           has no product and covers the first K read),
-    //                           the LDS store of tile j+2 and the global loads
-    //                           of tile j+3 early.
-    constexpr int kScore = 2 * NKB;
-    constexpr int kPairsV = 2 * NDB;           // V operands (db, kb)
-    constexpr int kSlots = kScore + 2 * kPairsV;
-    constexpr int kLookahead = 3;              // V operands read ahead
-    constexpr int kKAhead = 4;                 // K operands read ahead
-    constexpr int kStoreSlot = 1, kLoadSlot = 2;
-    // probability pair k (map k / 8, registers 2 (k % 8) and +1) starts in slot
-    auto pair_slot = [](int k) { return k * (kSlots - 3) / 16 - 1; };
-    static_assert(15 * (kSlots - 3) / 16 - 1 + 2 < kSlots, "pairs must finish in the slots");
+    // Issue plan of one iteration: kSlots slots, each holding one MFMA and a
+    // planned share of the vector work, fenced by scheduling barriers:
+    //   slots 0 .. NKB-1     score products of tile j+1 (K operands read
+    //                        before slot -1);
+    //   slots NKB ..         P.V products of tile j-1, each V operand read
+    //                        kLookahead products ahead;
+    //   vector work          the 8 probability pairs of tile j, each in three
+    //                        steps (scale, exp2, pack and sum) in consecutive
+    //                        slots so that a slot's work is independent,
+    //                        starting in a slot -1 that has no product; the
+    //                        LDS store of tile j+2 and the global loads of
+    //                        tile j+3 early.
+    constexpr int kPairsV = 2 * NDB;  // V operands (db, kb)
+    constexpr int kSlots = NKB + kPairsV;
+    constexpr int kLookahead = 3;
+    constexpr int kLoadSlot = 1;
+    // probability pair k (registers 2k, 2k+1) starts in slot pair_slot(k)
+    auto pair_slot = [](int k) { return k * (kSlots - 3) / 8 - 1; };
+    static_assert(7 * (kSlots - 3) / 8 - 1 + 2 < kSlots, "pairs must finish in the slots");
 
     // One iteration j (see the header); cur holds tile j, oth tile j-1 and
     // then j+1.  PREV: tile j-1 exists; NEXT: tile j+1 exists.
     auto iteration = [&](auto prev, auto next, int j, TileState& cur, TileState& oth) {
         constexpr bool PREV = decltype(prev)::value;
         constexpr bool NEXT = decltype(next)::value;
-        const float base1 = m1 == -INFINITY ? 0.f : m1;
-        const float base2 = m2 == -INFINITY ? 0.f : m2;
+        const float base = m == -INFINITY ? 0.f : m;
 
-        bf16x8 ka[kScore], va[kPairsV];
-        const uint16_t* k1s = smem + stage_of(j + 1) * C::kStage + krow * C::kKStride + 8 * lh;
-        // K operand i: map i % 2, channels 16 (i / 2) + 8 lh ..
-        auto read_k = [&](int i) {
-            ka[i] = *(const bf16x8*)(k1s + (i & 1) * C::kKElems + 16 * (i >> 1));
-        };
+        bf16x8 ka[NKB], va[kPairsV];
         if constexpr (NEXT) {
 #pragma unroll
-            for (int i = 0; i < kKAhead; ++i) read_k(i);
+            for (int kb = 0; kb < NKB; ++kb) ka[kb] = k_operand(stage_of(j + 1), kb);
         }
         const int vbuf = stage_of(j - 1);
         if constexpr (PREV) {
 #pragma unroll
             for (int q = 0; q < kLookahead; ++q) va[q] = v_operand(vbuf, q >> 1, q & 1);
         }
-        float t1a = 0.f, t1b = 0.f, t2a = 0.f, t2b = 0.f;
-        float xs[32];  // probabilities in flight, element 16 map + register
+        float ta = 0.f, tb = 0.f;
+        float xs[16];  // probabilities in flight, by accumulator register
         __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
         for (int slot = -1; slot < kSlots; ++slot) {
             if (slot < 0) {
-                // no product: the first K operands are still on their way
-            } else if (slot < kScore) {
-                if constexpr (NEXT) {
-                    const int kb = slot >> 1;
-                    if (slot + kKAhead < kScore) read_k(slot + kKAhead);
-                    if ((slot & 1) == 0)
-                        oth.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            ka[slot], qf1[kb], kb == 0 ? f32x16{} : oth.s1, 0, 0, 0);
-                    else
-                        oth.s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            ka[slot], qf2[kb], kb == 0 ? f32x16{} : oth.s2, 0, 0, 0);
-                }
+                // no product: the first operands are still on their way
+            } else if (slot < NKB) {
+                if constexpr (NEXT)
+                    oth.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        ka[slot], qf[slot], slot == 0 ? f32x16{} : oth.s, 0, 0, 0);
             } else {
                 if constexpr (PREV) {
-                    const int i = slot - kScore, q = i >> 1;
-                    if ((i & 1) == 0) {
-                        if (q + kLookahead < kPairsV)
-                            va[q + kLookahead] = v_operand(vbuf, (q + kLookahead) >> 1, (q + kLookahead) & 1);
-                        mfma_agpr(o1[q >> 1], va[q], oth.p1[q & 1]);
-                    } else {
-                        mfma_agpr(o2[q >> 1], va[q], oth.p2[q & 1]);
-                    }
+                    const int q = slot - NKB;
+                    if (q + kLookahead < kPairsV)
+                        va[q + kLookahead] =
+                            v_operand(vbuf, (q + kLookahead) >> 1, (q + kLookahead) & 1);
+                    o[q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[q], oth.p[q & 1],
+                                                                        o[q >> 1], 0, 0, 0);
                 }
             }
-            // probability pair k: scale at pair_slot(k), exp2 one slot later,
-            // sums and bf16 packing one slot after that, so that the work of
-            // a slot is independent and no chain latency stalls the wave
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int e = 2 * (k & 7);
-                const f32x16& sk = k < 8 ? cur.s1 : cur.s2;
-                const float bk = k < 8 ? base1 : base2;
+            for (int k = 0; k < 8; ++k) {
                 if (pair_slot(k) == slot) {
-                    xs[2 * k] = fmaf(sk[e], sl2, -bk);
-                    xs[2 * k + 1] = fmaf(sk[e + 1], sl2, -bk);
+                    xs[2 * k] = fmaf(cur.s[2 * k], sl2, -base);
+                    xs[2 * k + 1] = fmaf(cur.s[2 * k + 1], sl2, -base);
                 }
                 if (pair_slot(k) + 1 == slot) {
                     xs[2 * k] = __builtin_amdgcn_exp2f(xs[2 * k]);
                     xs[2 * k + 1] = __builtin_amdgcn_exp2f(xs[2 * k + 1]);
                 }
-                if (pair_slot(k) + 2 == slot) {
-                    if (k < 8)
-                        pack_pair(cur.p1, e, xs[2 * k], xs[2 * k + 1], (k & 1) ? t1b : t1a);
-                    else
-                        pack_pair(cur.p2, e, xs[2 * k], xs[2 * k + 1], (k & 1) ? t2b : t2a);
-                }
+                if (pair_slot(k) + 2 == slot)
+                    pack_pair(cur.p, 2 * k, xs[2 * k], xs[2 * k + 1], (k & 1) ? tb : ta);
             }
-            if (slot == kStoreSlot) store_tile(stage_of(j + 2));  // zeros once past the end
-            if (slot == kLoadSlot) load_tile(j + 3);
+            if (slot == kLoadSlot) issue_tile(j + C::kAhead);  // zeros once past the end
             __builtin_amdgcn_sched_barrier(0);
         }
         // Keep the common-path probabilities ahead of the rare branch below
         // (which forms them again) rather than sunk into its other side.
-        asm volatile("" ::"v"(cur.p1[0]), "v"(cur.p1[1]), "v"(cur.p2[0]), "v"(cur.p2[1]),
-                     "v"(t1a), "v"(t1b), "v"(t2a), "v"(t2b));
+        asm volatile("" ::"v"(cur.p[0]), "v"(cur.p[1]), "v"(ta), "v"(tb));
 
         // causal diagonal or ragged last tile: mask tile j+1 before its
         // probabilities are formed in the next iteration
         if constexpr (NEXT) {
-            if (j + 1 >= nfull) mask(j + 1, oth.s1, oth.s2);
+            if (j + 1 >= nfull) mask(j + 1, oth.s);
         }
         // lazy-maximum test on tile j: a large partial sum means that some
         // scores passed the stale maximum; take the exact maxima of the tile,
         // rescale, and form its probabilities again
-        float t1 = t1a + t1b, t2 = t2a + t2b;
-        if (__builtin_amdgcn_ballot_w64(t1 > kSumLimit || t2 > kSumLimit)) {
-            const float x1 = max16(cur.s1) * sl2, x2 = max16(cur.s2) * sl2;
-            const float mn1 = fmaxf(m1, fmaxf(x1, xor32(x1)));
-            const float mn2 = fmaxf(m2, fmaxf(x2, xor32(x2)));
-            const float al1 = mn1 == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m1 - mn1);
-            const float al2 = mn2 == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mn2);
-            m1 = mn1;
-            m2 = mn2;
-            l1 *= al1;
-            l2 *= al2;
-            mfma_drain<NDB>(o1, o2);
-            scale_acc<NDB>(o1, al1);
-            scale_acc<NDB>(o2, al2);
-            const float nb1 = m1 == -INFINITY ? 0.f : m1;
-            const float nb2 = m2 == -INFINITY ? 0.f : m2;
-            t1 = t2 = 0.f;
+        float tsum = ta + tb;
+        if (__builtin_amdgcn_ballot_w64(tsum > kSumLimit)) {
+            const float x = max16(cur.s) * sl2;
+            const float mn = fmaxf(m, fmaxf(x, xor32(x)));
+            const float al = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+            m = mn;
+            l *= al;
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                prob_pair(cur.s1, e, sl2, nb1, cur.p1, t1);
-                prob_pair(cur.s2, e, sl2, nb2, cur.p2, t2);
-            }
+            for (int db = 0; db < NDB; ++db) o[db] *= al;
+            const float nb = m == -INFINITY ? 0.f : m;
+            tsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) prob_pair(cur.s, e, sl2, nb, cur.p, tsum);
         }
-        l1 += t1;
-        l2 += t2;
+        l += tsum;
+        // tile j+2 (read from the next iteration on) must have landed; tiles
+        // j+3 .. j+kAhead may still be in flight
+        wait_loads(std::integral_constant<int, (C::kAhead - 2) * C::kLoads>{});
         __syncthreads();
     };
 
@@ -540,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     const bool_c<false> F;
     if (nkt == 1) {
         iteration(F, F, 0, A, B);
-        pv(stage_of(0), A.p1, A.p2);
+        pv(stage_of(0), A.p);
     } else {
         iteration(F, T, 0, A, B);
         // tile j lives in A for even j and in B for odd j
@@ -552,27 +517,42 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         if (j < nkt - 1) {
             iteration(T, T, j, B, A);
             iteration(T, F, j + 1, A, B);
-            pv(stage_of(j + 1), A.p1, A.p2);
+            pv(stage_of(j + 1), A.p);
         } else {
             iteration(T, F, j, B, A);
-            pv(stage_of(j), B.p1, B.p2);
+            pv(stage_of(j), B.p);
         }
     }
 
-    // epilogue: D = O1/l1 - lambda O2/l2, then GroupNorm over the dv channels
-    mfma_drain<NDB>(o1, o2);
-    const float lam = a.lam[h];
-    const float L1 = l1 + xor32(l1);
-    const float L2 = l2 + xor32(l2);
-    const float c1 = 1.f / L1;
-    const float c2 = lam / L2;
+    // epilogue: D = O1/l1 - lambda O2/l2 (the lambda map's product goes
+    // through LDS to the first map's wave), then GroupNorm over the dv
+    // channels and the (1 - lambda_init) scale
+    const float L = l + xor32(l);
+    // every wave is done with the tile ring, and no load (the last ones read
+    // past the end and write zeros) may land on the exchange area
+    wait_loads(std::integral_constant<int, 0>{});
+    __syncthreads();
+    float* xchg = (float*)smem;
+    float* my = xchg + qb * (NDB * 16 * 64) + lane;
+    if (map == 1) {
+        const float c2 = a.lam[h] / L;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) my[(db * 16 + r) * 64] = product(o[db][r], c2);
+        }
+    }
+    __syncthreads();
+    if (map == 1) return;
+
+    const float c1 = 1.f / L;
     float dsum = 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float dval = diff_of_products(o1[db][r], c1, o2[db][r], c2);
-            o1[db][r] = dval;
+            const float dval = diff_of_products(o[db][r], c1, my[(db * 16 + r) * 64], 1.f);
+            o[db][r] = dval;
             dsum += dval;
         }
     }
@@ -584,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float c = o1[db][r] - mean;
+                const float c = o[db][r] - mean;
                 vsum = fmaf(c, c, vsum);
             }
         }
@@ -594,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o1[db][r] = (o1[db][r] - mean) * scale;
+            for (int r = 0; r < 16; ++r) o[db][r] = (o[db][r] - mean) * scale;
         }
     }
 
@@ -606,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
             for (int g = 0; g < 4; ++g) {
                 bf16x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (__bf16)o1[db][4 * g + e];
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)o[db][4 * g + e];
                 *(bf16x4*)(orow + 32 * db + 8 * g + 4 * lh) = w;
             }
         }
