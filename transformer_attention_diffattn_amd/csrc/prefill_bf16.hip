@@ -15,20 +15,19 @@
 //   registers of a wave (one O^T accumulator, one score tile), which lets two
 //   waves share each SIMD; a wave waiting on LDS or on the barrier then
 //   leaves the SIMD to the other.  Waves w and w + 4 run on the same SIMD, one
-//   per map.  K1, K2 and V stream through a 4-stage LDS ring in tiles of 32
-//   keys; each wave reads the K tile of its own map and the shared V tile.
+//   per map.  K1, K2 and V stream through an 8-stage LDS ring in tiles of 32
+//   keys, loaded 6 tiles ahead of use; each wave reads the K tile of its own
+//   map and the shared V tile.
 //
 //   Iteration j of a wave issues, in one branch-free block,
 //     MFMA  scores of tile j+1, P.V of tile j-1;
 //     VALU  probabilities of tile j, row sums;
-//     memory  global loads of tile j+3, LDS stores of tile j+2 (all waves);
+//     memory  the global-to-LDS loads of tile j+6 (all waves);
 //   and ends with the masking of tile j+1 (tiles on the causal diagonal and
 //   the ragged last tile only) and the lazy-maximum test of tile j (below),
-//   whose body almost never runs.  Tile j-1's V is read in iteration j and
-//   tile j+1's K too, hence 4 stages; one barrier per tile.  The block is a
-//   fixed sequence of slots, one MFMA each with a planned share of the vector
-//   work, fenced by scheduling barriers so that the compiler cannot bunch the
-//   products together.
+//   whose body almost never runs.  None of the three streams waits for
+//   another inside the block, so the two waves of a SIMD can overlap one's
+//   matrix work with the other's vector work.  One barrier per tile.
 //
 // Per tile and wave, on MFMA v_mfma_f32_32x32x16_bf16 (k = the wave's map):
 //   S_k^T = K_k Q_k^T          (keys on the M axis, the wave's 32 queries on N),
@@ -68,12 +67,13 @@
 //   key e (of 4 consecutive keys) at channel base + 4r, so lane i gets channel
 //   base + i of those 4 keys; two such reads give the 8 keys of a k-slot half.
 //
-// LDS per stage: K1 and K2 row-major [32][d + 8] (the pad keeps the 16-byte
-// operand reads conflict-free), V row-major [32][dv + 32] (a 64-byte pad puts
-// the 4 rows a half-wave of transposing reads touches in distinct banks).
-// Global loads are raw buffer loads whose descriptor ends at the last key of
-// the (batch, head): rows past the end read as zeros without a branch or a
-// clamp, and their scores are masked, so they contribute nothing.
+// LDS per stage: K1, K2 and V tiles row-major without padding, 16-byte
+// chunks XOR-swizzled within each row (see k_swz, v_swz) so that operand
+// reads hit distinct banks.  Tiles are copied from global memory straight
+// into LDS by buffer loads with the LDS destination (no registers, no LDS
+// store instructions), through descriptors that end at the last key of the
+// (batch, head): rows past the end are filled with zeros without a branch or
+// a clamp, and their scores are masked, so they contribute nothing.
 
 #include "internal.h"
 
@@ -132,18 +132,25 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 // LDS tiles are stored without padding; 16-byte chunk ch of row r sits at
 // chunk position ch ^ swz(r) of its row, which spreads the rows an MFMA
-// operand read touches at once over distinct banks.  K operand reads take
-// rows {0,1,2,3,8,9,10,11} (+4, +16, ...) at one chunk column per 8 lanes;
-// transposing V reads take 4 consecutive rows at one 32-byte column per 16
-// lanes.
+// operand read touches at once over distinct banks.  The LDS serves 256 bytes
+// (64 banks) per cycle: 16 lanes of a 16-byte read, 32 lanes of an 8-byte
+// read.  A K operand read gives 16 lanes 16 different rows at one chunk
+// column; a transposing V read gives 32 lanes 4 consecutive rows at one
+// 64-byte column.  The swizzles make those land on distinct banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
     if constexpr (D == 64)
-        return (r & 3) | ((r >> 1) & 4);        // 8 chunks per row
+        return (r >> 1) & 7;  // 8 chunks per row, two rows per 256 bytes
     else
-        return ((r >> 1) & 1) | ((r >> 2) & 2);  // 4 chunks per row (two rows per 128 B)
+        return (r >> 2) & 3;  // 4 chunks per row, four rows per 256 bytes
 }
-__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+template <int DV>
+__device__ __forceinline__ int v_swz(int r) {
+    if constexpr (DV == 128)
+        return 4 * (r & 3);         // 16 chunks per row
+    else
+        return 4 * ((r >> 1) & 1);  // 8 chunks per row, two rows per 256 bytes
+}
 
 // a*b - c*d with both products rounded before the subtraction (no fused
 // multiply-add), so equal operands cancel to exactly zero
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         } else {
             const int pos = c0 - 2 * C::kKChunks + lane;
             const int row = pos / (DV / 8);
-            ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz(row));
+            ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz<DV>(row));
         }
     }
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;  // LDS byte address
@@ -330,19 +337,18 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     };
 
     // per-lane pieces of the transposing V read: row e of 4 (e = (lane%16)/4,
-    // plus 8 for the upper half-wave), channels 32 db + 16 (vg%2) + 4 (lane%4);
-    // under the swizzle the chunk of channel group (db, vg%2) moves to
-    // (4 db + c0) ^ 2e with c0 = 2 (vg%2) + (lane%4)/2, which is
-    // ((c0 ^ 2e) ^ 4 (db%2)) + 8 (db/2).
+    // plus 8 for the upper half-wave; further rows add multiples of 4, which
+    // the swizzle does not see), channels 32 db + 16 (vg%2) + 4 (lane%4),
+    // i.e. chunk 4 db + 2 (vg%2) + (lane%4)/2 and byte 8 (lane%2) in it
     const int vg = lane >> 4;
     const int ve = (lane & 15) >> 2;
-    const int vw = (2 * (vg & 1) + ((lane & 3) >> 1)) ^ (2 * ve);
     const int v_lane_row = 2 * C::kKElems + (8 * (vg >> 1) + ve) * DV + 4 * (lane & 1);
-    const int v_off_even = v_lane_row + 8 * vw;
-    const int v_off_odd = v_lane_row + 8 * (vw ^ 4);
+    int v_off[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        v_off[db] = v_lane_row + 8 * ((4 * db + 2 * (vg & 1) + ((lane & 3) >> 1)) ^ v_swz<DV>(ve));
     auto v_operand = [&](int buf, int db, int kb) {
-        const uint16_t* vp = smem + buf * C::kStage + ((db & 1) ? v_off_odd : v_off_even) +
-                             64 * (db >> 1) + 16 * kb * DV;
+        const uint16_t* vp = smem + buf * C::kStage + v_off[db] + 16 * kb * DV;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)vp);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -393,8 +399,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         m = fmaxf(x, xor32(x));
     }
 
-    // Issue plan of one iteration: kSlots slots, each holding one MFMA and a
-    // planned share of the vector work, fenced by scheduling barriers:
+    // Source order of one iteration: kSlots slots, each with one MFMA and a
+    // share of the vector work (the compiler's scheduler takes it from there):
     //   slots 0 .. NKB-1     score products of tile j+1 (K operands read
     //                        before slot -1);
     //   slots NKB ..         P.V products of tile j-1, each V operand read
@@ -403,8 +409,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     //                        steps (scale, exp2, pack and sum) in consecutive
     //                        slots so that a slot's work is independent,
     //                        starting in a slot -1 that has no product; the
-    //                        LDS store of tile j+2 and the global loads of
-    //                        tile j+3 early.
+    //                        loads of tile j+6 early.
     constexpr int kPairsV = 2 * NDB;  // V operands (db, kb)
     constexpr int kSlots = NKB + kPairsV;
     constexpr int kLookahead = 3;
@@ -432,7 +437,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         }
         float ta = 0.f, tb = 0.f;
         float xs[16];  // probabilities in flight, by accumulator register
-        __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
         for (int slot = -1; slot < kSlots; ++slot) {
@@ -466,7 +470,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
                     pack_pair(cur.p, 2 * k, xs[2 * k], xs[2 * k + 1], (k & 1) ? tb : ta);
             }
             if (slot == kLoadSlot) issue_tile(j + C::kAhead);  // zeros once past the end
-            __builtin_amdgcn_sched_barrier(0);
         }
         // Keep the common-path probabilities ahead of the rare branch below
         // (which forms them again) rather than sunk into its other side.
