@@ -179,7 +179,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # a few hundred launches let the GPU reach its steady clocks before timing
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -250,7 +251,7 @@ def main():
     if not args.no_decode:
         wd = workloads.get("decode_bf16")
         dec_steps = max(5, args.steps // 5)
-        dms, splits, ws_bytes = bench_decode(wd, dec_steps, max(2, args.warmup // 2))
+        dms, splits, ws_bytes = bench_decode(wd, dec_steps, max(2, args.warmup // 30))
         nbytes = wd.algorithmic_bytes()
         gbs = nbytes / (dms * 1e-3) / 1e9
         rec["decode"] = {

@@ -285,7 +285,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     auto stage_of = [](int kt) { return kt & (C::kStages - 1); };
     auto issue_tile = [&](int kt) {
         const int64_t key0 = (int64_t)kt * kBc;
-        const int64_t left = (int64_t)a.Nk - key0;
+        // tiles past this workgroup's last one get an empty descriptor: the
+        // instruction count per tile stays fixed (the waits count on it) and
+        // the lanes just write zeros, without touching memory
+        const int64_t left = kt < nkt ? (int64_t)a.Nk - key0 : 0;
         const uint32_t stage = smem_base + 2u * (uint32_t)(stage_of(kt) * C::kStage);
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
@@ -386,9 +389,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     };
     TileState A, B;
 
-    // prologue: tiles 0 .. kAhead-1 in flight; tiles 0 and 1 complete
+    // prologue: tiles 0 .. kAhead-1 in flight; tiles 0 and 1 complete.  The
+    // compiler waits for the Q loads before their first use by counting only
+    // its own loads, which would also drain every tile load issued before that
+    // use; so the Q fragments are taken (and waited for) right after tiles 0
+    // and 1, which the first iteration needs anyway, and the rest follow.
+    issue_tile(0);
+    issue_tile(1);
 #pragma unroll
-    for (int t0 = 0; t0 < C::kAhead; ++t0) issue_tile(t0);
+    for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(qf[kb]));
+#pragma unroll
+    for (int t0 = 2; t0 < C::kAhead; ++t0) issue_tile(t0);
     wait_loads(std::integral_constant<int, (C::kAhead - 2) * C::kLoads>{});
     __syncthreads();
     scores(0, A.s);
