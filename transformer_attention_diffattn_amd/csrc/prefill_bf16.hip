@@ -213,7 +213,7 @@ __device__ __forceinline__ void prob_pair(const f32x16& s, int e, float sl2, flo
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
-template <int D, int DV, bool CAUSAL>
+template <int D, int DV, bool CAUSAL, bool FLAT>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     using C = Cfg<D, DV>;
     constexpr int NDB = DV / 32;
@@ -283,24 +283,48 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     }
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;  // LDS byte address
     auto stage_of = [](int kt) { return kt & (C::kStages - 1); };
+    // FLAT: every tensor of the (batch, head) spans < 2 GiB, so one descriptor
+    // per load instruction, built here, covers it and a tile is a byte offset
+    // added to the lane offsets; otherwise each tile gets its own descriptor.
+    i32x4 rs[C::kLoads];
+    uint32_t tile_bytes[C::kLoads], region_bytes[C::kLoads];
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+        const int c0 = 64 * (wave_u + i * (kThreads / 64));
+        const bool in_k = c0 < 2 * C::kKChunks;
+        const uint16_t* base = in_k ? (c0 < C::kKChunks ? gk1 : gk2) : gv;
+        const int64_t bytes = (int64_t)a.Nk * (in_k ? D : DV) * 2;
+        rs[i] = sgpr_rsrc(base, bytes);
+        tile_bytes[i] = kBc * (in_k ? D : DV) * 2;
+        region_bytes[i] = FLAT ? (uint32_t)bytes : 0u;
+    }
     auto issue_tile = [&](int kt) {
-        const int64_t key0 = (int64_t)kt * kBc;
-        // tiles past this workgroup's last one get an empty descriptor: the
-        // instruction count per tile stays fixed (the waits count on it) and
-        // the lanes just write zeros, without touching memory
-        const int64_t left = kt < nkt ? (int64_t)a.Nk - key0 : 0;
         const uint32_t stage = smem_base + 2u * (uint32_t)(stage_of(kt) * C::kStage);
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
             const int c0 = 64 * (wave_u + i * (kThreads / 64));
-            const bool in_k = c0 < 2 * C::kKChunks;
-            const uint16_t* base = in_k ? (c0 < C::kKChunks ? gk1 : gk2) + key0 * D : gv + key0 * DV;
-            const i32x4 rsrc = sgpr_rsrc(base, left * (in_k ? D : DV) * 2);
             const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + 16u * (uint32_t)c0);
-            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                         :
-                         : "s"(m0), "v"(ld_off[i]), "s"(rsrc)
-                         : "memory", "m0");
+            // Tiles past this workgroup's last one read out of range: the
+            // instruction count per tile stays fixed (the waits count on it)
+            // and the lanes just write zeros, without touching memory.
+            if constexpr (FLAT) {
+                const uint32_t toff = kt < nkt ? (uint32_t)kt * tile_bytes[i] : region_bytes[i];
+                asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                             :
+                             : "s"(m0), "v"(ld_off[i] + toff), "s"(rs[i])
+                             : "memory", "m0");
+            } else {
+                const int64_t key0 = (int64_t)kt * kBc;
+                const int64_t left = kt < nkt ? (int64_t)a.Nk - key0 : 0;
+                const bool in_k = c0 < 2 * C::kKChunks;
+                const uint16_t* base =
+                    in_k ? (c0 < C::kKChunks ? gk1 : gk2) + key0 * D : gv + key0 * DV;
+                const i32x4 rsrc = sgpr_rsrc(base, left * (in_k ? D : DV) * 2);
+                asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                             :
+                             : "s"(m0), "v"(ld_off[i]), "s"(rsrc)
+                             : "memory", "m0");
+            }
         }
     };
     // The loads above are invisible to the compiler's counters: before the
@@ -613,8 +637,12 @@ hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)nqt * a.B * a.H));
     PrefillArgs copy = a;
     void* args[] = {&copy};
-    const void* fn = causal ? (const void*)prefill_bf16_kernel<D, DV, true>
-                            : (const void*)prefill_bf16_kernel<D, DV, false>;
+    // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
+    const bool flat = (int64_t)a.Nk * DV * 2 + 64 * 1024 < (int64_t)0x7fffffff;
+    const void* fn = causal ? (flat ? (const void*)prefill_bf16_kernel<D, DV, true, true>
+                                    : (const void*)prefill_bf16_kernel<D, DV, true, false>)
+                            : (flat ? (const void*)prefill_bf16_kernel<D, DV, false, true>
+                                    : (const void*)prefill_bf16_kernel<D, DV, false, false>);
     return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, stream);
 }
 
