@@ -97,6 +97,26 @@ def test_prefill_pre_norm_output(dtype):
     assert_close(out, ref, w.torch_dtype, "pre-norm D")
 
 
+# More (query tile, head) items than compute units: each workgroup of the
+# bf16 kernel runs several items in turn, reusing its LDS ring, and the items
+# it gets differ in length (causal) or are very short (few keys).
+@pytest.mark.parametrize("d,dv,B,H,nq,nk,causal,pre_norm", [
+    (64, 128, 1, 300, 40, 40, True, False),
+    (64, 128, 2, 64, 700, 700, True, False),
+    (64, 128, 1, 260, 97, 97, False, True),
+    (64, 128, 3, 100, 257, 257, False, False),
+    (64, 128, 1, 200, 300, 700, False, False),
+    (32, 64, 1, 300, 40, 40, False, False),
+    (32, 64, 2, 64, 700, 700, False, False),
+    (32, 64, 1, 260, 97, 97, True, True),
+    (32, 64, 3, 100, 257, 257, True, False),
+], ids=lambda v: str(v))
+def test_prefill_many_items_per_workgroup(d, dv, B, H, nq, nk, causal, pre_norm):
+    w = _custom(B, H, nq, nk, d, dv, "bf16", causal, seed=B * 1000 + H + nq)
+    out, ref = _run_prefill_full_compare(w, pre_norm=pre_norm)
+    assert_close(out, ref, w.torch_dtype, f"d{d} B{B} H{H} nq{nq} nk{nk} causal={causal}")
+
+
 def test_tiny_noncausal_f32_workload():
     w = workloads.get("tiny_noncausal_f32")
     out, ref = _run_prefill_full_compare(w)

@@ -9,6 +9,23 @@
 #include <mutex>
 
 namespace diffattn {
+
+// Compute units of the current device, cached per device.
+int device_cus() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> g(mu);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -33,22 +50,6 @@ int check_dims(const diffattn_dims* dm) {
 }
 
 float scale_log2(int d) { return (float)(1.4426950408889634 / sqrt((double)d)); }
-
-// Compute units of the current device, cached per device.
-int device_cus() {
-    static std::mutex mu;
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    std::lock_guard<std::mutex> g(mu);
-    if (cache[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cache[dev] = cus;
-    }
-    return cache[dev];
-}
 
 // Keys per split, rounded to whole 128-key blocks.
 int32_t split_chunk(int32_t L, int32_t splits) {

@@ -54,6 +54,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);
 
+// Compute units of the current device (cached per device); 0 if unknown.
+int device_cus();
+
 // Size in floats of one split's partial record: m1, l1, m2, l2, O1[dv], O2[dv].
 __host__ __device__ inline int64_t decode_record_floats(int dv) { return 4 + 2 * (int64_t)dv; }
 

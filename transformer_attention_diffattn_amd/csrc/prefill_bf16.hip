@@ -8,7 +8,11 @@
 // one memory pass ("Throughput and Hardware Realities"); this is that kernel.
 //
 // Work decomposition
-//   One workgroup = 8 wavefronts = 128 query rows of one (batch, head).  Wave
+//   A work item is 128 query rows of one (batch, head), taken by one
+//   workgroup of 8 wavefronts.  The grid is persistent (one workgroup per
+//   compute unit when there are more items than units): items are sorted
+//   longest-first and dealt out in a snake, so the causal lengths even out
+//   and no workgroup launches per item.  Wave
 //   w owns query block w % 4 (32 rows) of map w / 4: the two softmax maps of
 //   a row are computed by two waves, and the lambda-weighted subtraction is
 //   done once, through LDS, in the epilogue.  Splitting by map halves the
@@ -36,7 +40,9 @@
 //   l and l+32), so online-softmax row statistics are in-lane reductions plus
 //   one exchange, and the rescale of O^T is a per-lane scalar.  The epilogue
 //   forms D = O_1 / l_1 - lambda O_2 / l_2, the per-head GroupNorm over the dv
-//   channels and the (1 - lambda_init) scale.
+//   channels and the (1 - lambda_init) scale; the two waves of a query block
+//   each finish half of the channels and exchange half-row statistics, and
+//   the output goes out through LDS as whole row segments.
 //
 // Online softmax with a lazy maximum: the running maximum m of a row is set
 // exactly from the first tile and afterwards moves only when needed.  Each
@@ -118,10 +124,15 @@ struct Cfg {
     // a stage is refilled kStages - kAhead tiles after the barrier that ends
     // its last reads (V of tile t is read in iteration t + 1)
     static_assert(kAhead + 2 <= kStages, "ring too small for the load distance");
-    // epilogue exchange: one float per (query block, accumulator, lane)
-    static constexpr int kXchgFloats = kBlocks * (DV / 32) * 16 * 64;
-    static constexpr int kSmemElems =
-        kStages * kStage > 2 * kXchgFloats ? kStages * kStage : 2 * kXchgFloats;
+    // epilogue, reusing the ring: the two half-row exchanges (one float per
+    // query block, accumulator and lane), the GroupNorm statistics (two
+    // floats per wave and lane) and the bf16 output staging (32 rows by DV/2
+    // channels per wave), in bf16 elements
+    static constexpr int kXchgElems = 2 * kBlocks * (DV / 32) * 16 * 64;
+    static constexpr int kStatElems = 4 * (kThreads / 64) * 64;
+    static constexpr int kStageOutElems = (kThreads / 64) * 32 * (DV / 2);
+    static constexpr int kEpiElems = kXchgElems + kStatElems + kStageOutElems;
+    static constexpr int kSmemElems = kStages * kStage > kEpiElems ? kStages * kStage : kEpiElems;
 };
 
 __device__ __forceinline__ int swap23(int r) {
@@ -220,21 +231,38 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     constexpr int NKB = D / 16;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::kSmemElems];
 
-    const int tid = threadIdx.x;
+
+    // Work items (query tile, batch*head), longest causal tiles first: item k
+    // takes query tile t = k / BH (counted from the last one) of head k % BH.
+    // The grid is persistent: in round r workgroup w takes item r G + w for
+    // even r and r G + w' for odd r, a snake over the sorted items that evens
+    // out the causal lengths.  Workgroups are dealt to the 8 XCDs round-robin,
+    // so w' reverses w's slot within its XCD (w' = w mod 8 + 8 (G/8 - 1 -
+    // w/8)): every item of a head then runs on one XCD and its K/V on one L2.
+    const int BH = a.B * a.H;
+    const int nqt = (a.Nq + C::kBr - 1) / C::kBr;
+    const int n_items = nqt * BH;
+    const int G = gridDim.x;
+    const int w_even = blockIdx.x;
+    const int w_odd = (G & 7) == 0 ? (w_even & 7) + 8 * (G / 8 - 1 - w_even / 8) : G - 1 - w_even;
+    for (int r = 0;; ++r) {
+    const int k_item = r * G + ((r & 1) ? w_odd : w_even);
+    if (k_item >= n_items) break;
+    // opaque per item, so that nothing derived from the lane is hoisted out of
+    // the item loop and held live across it
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int lh = lane >> 5;
     const int qb = wave & (kBlocks - 1);  // query block
     const int map = wave >> 2;            // 0: first softmax map, 1: the lambda map
-
-    // longest causal tiles first: the first B*H blocks take the last query tile
-    const int BH = a.B * a.H;
-    const int nqt = (a.Nq + C::kBr - 1) / C::kBr;
-    const int t = blockIdx.x / BH;
-    const int bh = blockIdx.x - t * BH;
+    const int t = k_item / BH;
+    const int bh = k_item - t * BH;
     const int qt = CAUSAL ? (nqt - 1 - t) : t;
     const int h = bh % a.H;
+    const float lam_h = a.lam[h];
 
     const uint16_t* gq = (const uint16_t*)(map ? a.q2 : a.q1) + (size_t)bh * a.Nq * D;
     const uint16_t* gk1 = (const uint16_t*)a.k1 + (size_t)bh * a.Nk * D;
@@ -562,79 +590,124 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         }
     }
 
-    // epilogue: D = O1/l1 - lambda O2/l2 (the lambda map's product goes
-    // through LDS to the first map's wave), then GroupNorm over the dv
-    // channels and the (1 - lambda_init) scale
+    // epilogue: D = O1/l1 - lambda O2/l2, then GroupNorm over the dv channels
+    // and the (1 - lambda_init) scale.  The two waves of a query block (one
+    // per map) each finish half of the channels: the first map's wave the
+    // accumulator blocks [0, NH), the lambda map's wave [NH, NDB).  Each sends
+    // its scaled other half through LDS, forms D on its own half, and the
+    // GroupNorm statistics are merged from the two halves' means and centred
+    // sums of squares (pairwise merge of Chan, Golub and LeVeque).
+    constexpr int NH = NDB / 2;
     const float L = l + xor32(l);
     // every wave is done with the tile ring, and no load (the last ones read
-    // past the end and write zeros) may land on the exchange area
+    // past the end and write zeros) may land on the epilogue's areas
     wait_loads(std::integral_constant<int, 0>{});
     __syncthreads();
+    const int other = map ^ 1;
+    const float cs = map ? lam_h / L : 1.f / L;
     float* xchg = (float*)smem;
-    float* my = xchg + qb * (NDB * 16 * 64) + lane;
-    if (map == 1) {
-        const float c2 = a.lam[h] / L;
+    {
+        float* dst = xchg + (qb * 2 + other) * (NH * 16 * 64) + lane;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NH; ++db) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) my[(db * 16 + r) * 64] = product(o[db][r], c2);
+            for (int r = 0; r < 16; ++r)
+                dst[(db * 16 + r) * 64] = product(map ? o[db][r] : o[NH + db][r], cs);
         }
     }
     __syncthreads();
-    if (map == 1) return;
-
-    const float c1 = 1.f / L;
-    float dsum = 0.f;
+    float x[NH][16];
+    {
+        const float* src = xchg + (qb * 2 + map) * (NH * 16 * 64) + lane;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NH; ++db) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float dval = diff_of_products(o[db][r], c1, my[(db * 16 + r) * 64], 1.f);
-            o[db][r] = dval;
-            dsum += dval;
+            for (int r = 0; r < 16; ++r) {
+                const float got = src[(db * 16 + r) * 64];
+                const float own = map ? o[NH + db][r] : o[db][r];
+                x[db][r] = map ? diff_of_products(got, 1.f, own, cs)
+                               : diff_of_products(own, cs, got, 1.f);
+            }
         }
     }
     if (!(a.flags & 1u)) {
-        dsum += xor32(dsum);
-        const float mean = dsum * (1.f / DV);
-        float vsum = 0.f;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NH; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ps[r & 3] += x[db][r];
+        }
+        float hs = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        hs += xor32(hs);
+        const float mh = hs * (2.f / DV);  // mean of this half of the row
+        float pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < NH; ++db) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float c = o[db][r] - mean;
-                vsum = fmaf(c, c, vsum);
+                const float c = x[db][r] - mh;
+                pq[r & 3] = fmaf(c, c, pq[r & 3]);
             }
         }
-        vsum += xor32(vsum);
-        const float var = vsum * (1.f / DV);
+        float hq = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+        hq += xor32(hq);
+        float2* stats = (float2*)(smem + C::kXchgElems);
+        stats[(qb * 2 + map) * 64 + lane] = make_float2(mh, hq);
+        __syncthreads();
+        const float2 ot = stats[(qb * 2 + other) * 64 + lane];
+        // both waves evaluate the same expressions in the same order
+        const float mean = 0.5f * (mh + ot.x);
+        const float dm = mh - ot.x;
+        const float m2 = (hq + ot.y) + dm * dm * (0.25f * DV);
+        const float var = m2 * (1.f / DV);
         const float scale = (1.f - a.lambda_init) / sqrtf(var + a.eps);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NH; ++db) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] = (o[db][r] - mean) * scale;
+            for (int r = 0; r < 16; ++r) x[db][r] = (x[db][r] - mean) * scale;
         }
     }
 
-    if (qrow < a.Nq) {
-        __bf16* orow = gout + (size_t)qrow * DV;
+    // Output: the wave's 32 rows by DV/2 channels go through LDS (bf16, rows
+    // of kCpr 16-byte chunks, chunk index swizzled by the row's 256-byte line)
+    // so that each store instruction writes whole row segments.
+    {
+        constexpr int kCpr = DV / 16;       // chunks per half row
+        constexpr int kRpl = 256 / DV;      // half rows per 256 bytes
+        uint16_t* so = smem + C::kXchgElems + C::kStatElems + wave * (32 * (DV / 2));
+        const int swr = (l32 / kRpl) % kCpr;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NH; ++db) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 bf16x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (__bf16)o[db][4 * g + e];
-                *(bf16x4*)(orow + 32 * db + 8 * g + 4 * lh) = w;
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)x[db][4 * g + e];
+                *(bf16x4*)(so + l32 * (DV / 2) + 8 * ((4 * db + g) ^ swr) + 4 * lh) = w;
             }
         }
+        constexpr int kRowsPerStore = 64 / kCpr;
+        __bf16* gbase = gout + (size_t)wq0 * DV + map * (DV / 2);
+#pragma unroll
+        for (int k = 0; k < 32 / kRowsPerStore; ++k) {
+            const int row = k * kRowsPerStore + lane / kCpr;
+            const int ch = lane % kCpr;
+            const uint4 w = *(const uint4*)(so + row * (DV / 2) + 8 * (ch ^ ((row / kRpl) % kCpr)));
+            if (wq0 + row < a.Nq) *(uint4*)(gbase + (size_t)row * DV + 8 * ch) = w;
+        }
+    }
+    __syncthreads();  // the LDS ring and exchange area are reused by the next item
     }
 }
 
 template <int D, int DV>
 hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
     const int nqt = (a.Nq + Cfg<D, DV>::kBr - 1) / Cfg<D, DV>::kBr;
-    const dim3 grid((unsigned)((int64_t)nqt * a.B * a.H));
+    const int64_t items = (int64_t)nqt * a.B * a.H;
+    // item indices (and the snake's r * G + w) stay in int range
+    if (items > (int64_t)0x7fffffff - 4096) return hipErrorInvalidValue;
+    const int cus = device_cus();
+    const dim3 grid((unsigned)(cus > 0 && items > cus ? cus : items));
     PrefillArgs copy = a;
     void* args[] = {&copy};
     // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
