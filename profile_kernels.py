@@ -236,6 +236,13 @@ def _counter_cmd(out: str, i: int, workload: str):
             "--warmup", "1", "--no-cpu", "--no-decode", "--workload", workload]
 
 
+def prefill_kernel_of(workload: str) -> str:
+    """The prefill kernel bench.py runs on `workload` (head_dim 128: the wide one)."""
+    sys.path.insert(0, ROOT)
+    import workloads
+    return "prefill_bf16_wide_kernel" if workloads.get(workload).d == 128 else "prefill_bf16_kernel"
+
+
 def counters(out: str, workload: str = "causal_prefill_bf16") -> None:
     """Runs the counter passes of COUNTER_PASSES over bench.py on one workload."""
     out = os.path.abspath(out)
@@ -247,7 +254,7 @@ def counters(out: str, workload: str = "causal_prefill_bf16") -> None:
         with open(os.path.join(out, f"counters{i}.log"), "w") as log:
             subprocess.run(cmd, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT,
                            timeout=240, check=True)
-    counters_summarize(out, workload)
+    counters_summarize(out, workload, prefill_kernel_of(workload))
 
 
 def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
@@ -260,7 +267,8 @@ def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
         per = defaultdict(lambda: defaultdict(float))
         with open(_find(out, f"counters{i}", "counter_collection.csv")) as f:
             for r in csv.DictReader(f):
-                if _short(r["Kernel_Name"]) == kernel:
+                n = r["Kernel_Name"]
+                if f"{kernel}<" in n or n == kernel or f"::{kernel}" in n:
                     per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
         for name, disp in per.items():
             vals[name] = sum(disp.values()) / len(disp)
@@ -286,7 +294,8 @@ def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
         derived["exp (TRANS) instructions per MFMA"] = (
             vals.get("SQ_INSTS_VALU_TRANS_F32", 0) / vals["SQ_INSTS_MFMA"])
         derived["LDS instructions per MFMA"] = vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"]
-    src = KERNELS.get(kernel, (None, "prefill_bf16.hip"))[1]
+    src = {"prefill_bf16_wide_kernel": "prefill_bf16_wide.hip"}.get(
+        kernel, KERNELS.get(kernel, (None, "prefill_bf16.hip"))[1])
     lines = [f"# {kernel} on {workload}: SQ counters per dispatch", "",
              "Commands (from /tmp, TMPDIR=/tmp; written by "
              f"`python3 profile_kernels.py counters --workload {workload}`):", ""]
@@ -342,4 +351,4 @@ if __name__ == "__main__":
     elif a.action == "counters":
         counters(a.out, a.workload)
     else:
-        counters_summarize(a.out, a.workload)
+        counters_summarize(a.out, a.workload, prefill_kernel_of(a.workload))

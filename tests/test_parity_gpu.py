@@ -182,7 +182,8 @@ def test_deterministic_and_canary():
 # --------------------------------------------------------------------------
 
 def _sample_rows(n, rng, extra=()):
-    base = {0, 1, 63, 64, 127, 128, 129, n // 2, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1}
+    base = {0, 1, 2, 3, 5, 10, 31, 63, 64, 127, 128, 129, n // 2, n - 129, n - 128, n - 65, n - 64,
+            n - 2, n - 1}
     base |= set(int(e) for e in extra)
     base |= set(rng.integers(0, n, 6).tolist())
     return sorted(r for r in base if 0 <= r < n)

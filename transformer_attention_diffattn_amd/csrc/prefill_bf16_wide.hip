@@ -51,7 +51,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kBc = 32;                 // keys per tile
-constexpr float kRescaleLog2 = 8.0f;    // lazy-maximum slack, log2 units
+constexpr float kRescaleLog2 = 30.0f;   // lazy-maximum slack, log2 units (see maybe_rescale)
 
 template <int D, int DV>
 struct Cfg {
@@ -112,7 +112,12 @@ __device__ __forceinline__ void scale_acc(f32x16 (&o)[NDB], float alpha) {
     }
 }
 
-// Moves the running maximum of one map when some row needs it (lazy rule).
+// Moves the running maximum of one map when some row needs it (lazy rule):
+// only when a score exceeds the running maximum by more than 2^kRescaleLog2
+// in probability.  Probabilities up to 2^30 keep l and O far inside fp32
+// (O <= 2^30 * keys * max|V|) and lose nothing in bf16, whose precision is
+// relative; heavy-tailed scores, whose row maxima creep up tile after tile,
+// then almost never pay for the rescale of the 256 accumulators.
 template <int NDB>
 __device__ __forceinline__ void maybe_rescale(float mx, float& m, float& l, f32x16 (&o)[NDB]) {
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2)) {
