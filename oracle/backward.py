@@ -1,0 +1,123 @@
+"""fp64 CPU oracle for the gradient of the Differential Attention operator.
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: only the tests, the
+smoke check and the benchmark's CPU-baseline leg may use it, and it never
+imports the GPU library.
+
+The pages treat the operator as trained: lambda is a learnable scalar
+(iloveeagents.com, "Mathematical Formula"), and the GroupNorm with the
+(1 - lambda_init) scale of step 4 on llmbytes.dev ("How Differential Attention
+Cancels Common-Mode Noise") is there for stable gradient flow.  The gradient
+below is the chain rule taken through that same forward definition, written
+out step by step in the forward's notation (per batch entry b and head h,
+scale tau = 1/sqrt(d), c = 1 - lambda_init):
+
+  forward:  S_k = tau Q_k K_k^T (causal: keys after the query masked),
+            A_k = softmax_rows(S_k),  O_k = A_k V,  D = O_1 - lambda O_2,
+            y = c (D - mu) / sigma   (mu, sigma^2 + eps: mean and population
+            variance of each row of D over its dv channels);
+  backward, given dy:
+            dD = (1/sigma) (g - mean(g) - xhat mean(g xhat)),  g = c dy,
+                 xhat = (D - mu)/sigma   (dD = dy when the output is D itself);
+            dV = A_1^T dD - lambda A_2^T dD;
+            dA_1 = dD V^T,  dA_2 = -lambda dD V^T;
+            dS_k = A_k * (dA_k - rowsum(A_k * dA_k))     (softmax Jacobian);
+            dQ_k = tau dS_k K_k,  dK_k = tau dS_k^T Q_k;
+            dlambda = -sum(O_2 * dD)  (summed over rows; over b for the head).
+
+Dense N x N maps are materialised, so this is for the small shapes the tests
+use.  ``head_lse`` gives the natural-log log-sum-exp of each score row, the
+per-row softmax statistic a training forward keeps for the backward.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu").to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _scores(q, k, causal: bool) -> np.ndarray:
+    s = (q @ k.T) / np.sqrt(q.shape[1])
+    if causal:
+        nq, nk = s.shape
+        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], s, -np.inf)
+    return s
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def head_lse(q, k, *, causal: bool) -> np.ndarray:
+    """log(sum_j exp(S_ij)) of each row of one map's scores, fp64 [Nq]."""
+    s = _scores(_f64(q), _f64(k), causal)
+    m = s.max(axis=1)
+    return m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+
+
+def head_backward(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
+                  lambda_init: float = 0.8, eps: float = 1e-5, pre_norm: bool = False):
+    """Gradients of sum(dout * out) for one head.  Returns
+    (dq1, dq2, dk1, dk2, dv, dlam) in fp64; dlam is this head's scalar."""
+    q1, q2, k1, k2, v, dout = (_f64(t) for t in (q1, q2, k1, k2, v, dout))
+    d = q1.shape[1]
+    tau = 1.0 / np.sqrt(d)
+    a1 = _softmax_rows(_scores(q1, k1, causal))
+    a2 = _softmax_rows(_scores(q2, k2, causal))
+    o1, o2 = a1 @ v, a2 @ v
+    D = o1 - lam * o2
+    if pre_norm:
+        dD = dout
+    else:
+        mu = D.mean(axis=1, keepdims=True)
+        sigma = np.sqrt(((D - mu) ** 2).mean(axis=1, keepdims=True) + eps)
+        xhat = (D - mu) / sigma
+        g = (1.0 - lambda_init) * dout
+        dD = (g - g.mean(axis=1, keepdims=True)
+              - xhat * (g * xhat).mean(axis=1, keepdims=True)) / sigma
+    dv = a1.T @ dD - lam * (a2.T @ dD)
+    da1 = dD @ v.T
+    da2 = -lam * da1
+    ds1 = a1 * (da1 - (a1 * da1).sum(axis=1, keepdims=True))
+    ds2 = a2 * (da2 - (a2 * da2).sum(axis=1, keepdims=True))
+    dq1, dq2 = tau * (ds1 @ k1), tau * (ds2 @ k2)
+    dk1, dk2 = tau * (ds1.T @ q1), tau * (ds2.T @ q2)
+    dlam = -float((o2 * dD).sum())
+    return dq1, dq2, dk1, dk2, dv, dlam
+
+
+def backward(q1, q2, k1, k2, v, lam, dout, *, causal: bool, lambda_init: float = 0.8,
+             eps: float = 1e-5, pre_norm: bool = False):
+    """Whole batch: q*, k* [B,H,N,d], v and dout [B,H,N,dv], lam [H] (or a
+    scalar).  Returns fp64 (dq1, dq2, dk1, dk2, dv [B,H,N,*], dlam [H])."""
+    q1, q2, k1, k2, v, dout = (_f64(t) for t in (q1, q2, k1, k2, v, dout))
+    B, H = q1.shape[:2]
+    lam = np.broadcast_to(_f64(lam).reshape(-1), (H,))
+    grads = [np.zeros_like(t) for t in (q1, q2, k1, k2, v)]
+    dlam = np.zeros(H)
+    for b in range(B):
+        for h in range(H):
+            r = head_backward(q1[b, h], q2[b, h], k1[b, h], k2[b, h], v[b, h], float(lam[h]),
+                              dout[b, h], causal=causal, lambda_init=lambda_init, eps=eps,
+                              pre_norm=pre_norm)
+            for gbuf, gval in zip(grads, r[:5]):
+                gbuf[b, h] = gval
+            dlam[h] += r[5]
+    return (*grads, dlam)
+
+
+def lse(q, k, *, causal: bool) -> np.ndarray:
+    """head_lse over a batch: q, k [B,H,N,d] -> fp64 [B,H,Nq]."""
+    q, k = _f64(q), _f64(k)
+    B, H = q.shape[:2]
+    out = np.empty((B, H, q.shape[2]))
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = head_lse(q[b, h], k[b, h], causal=causal)
+    return out

@@ -1,0 +1,154 @@
+"""Pins of the fp64 backward oracle (oracle/backward.py) to facts other than
+itself (CPU only).
+
+* torch's autograd, differentiating the forward assembled from library
+  routines only -- scaled_dot_product_attention for each softmax map (the
+  DiffAttn formula, iloveeagents.com "Mathematical Formula") and group_norm
+  with one group per head for step 4 on llmbytes.dev -- must give the same six
+  gradients, causal and not, with and without the normalisation;
+* central finite differences of the C forward oracle along random directions
+  (every input tensor and lambda) must match the directional derivatives;
+* exp(S - lse) applied to V must equal scaled_dot_product_attention, and each
+  such row must sum to one;
+* lambda = 0 leaves map 2 without any gradient.
+
+A separate test plants mistakes in copies of the backward oracle and requires
+each copy to fail the autograd comparison.
+"""
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import backward as obw
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "backward.py")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _case(nq, d, dv, seed):
+    return dict(q1=_rand((nq, d), seed), q2=_rand((nq, d), seed + 1), k1=_rand((nq, d), seed + 2),
+                k2=_rand((nq, d), seed + 3), v=_rand((nq, dv), seed + 4),
+                dout=_rand((nq, dv), seed + 5))
+
+
+def _autograd(c, lam, causal, lambda_init, eps, pre_norm):
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in c.items()
+         if k != "dout"}
+    lam_t = torch.tensor(lam, dtype=torch.float64, requires_grad=True)
+    o1 = F.scaled_dot_product_attention(t["q1"][None], t["k1"][None], t["v"][None], is_causal=causal)[0]
+    o2 = F.scaled_dot_product_attention(t["q2"][None], t["k2"][None], t["v"][None], is_causal=causal)[0]
+    D = o1 - lam_t * o2
+    y = D if pre_norm else (1.0 - lambda_init) * F.group_norm(D, 1, eps=eps)
+    (y * torch.tensor(c["dout"])).sum().backward()
+    return [t[k].grad.numpy() for k in ("q1", "q2", "k1", "k2", "v")] + [float(lam_t.grad)]
+
+
+def check_against_autograd(bw):
+    for (nq, d, dv, lam, causal, pre_norm, seed) in [
+            (9, 4, 6, 0.5, False, False, 1), (9, 4, 6, 0.5, True, False, 2),
+            (17, 8, 16, 0.8, True, False, 3), (17, 8, 16, -0.3, False, True, 4),
+            (12, 6, 10, 1.2, True, True, 5), (1, 4, 6, 0.7, True, False, 6)]:
+        c = _case(nq, d, dv, seed)
+        got = bw.head_backward(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], lam, c["dout"],
+                               causal=causal, lambda_init=0.8, eps=1e-5, pre_norm=pre_norm)
+        want = _autograd(c, lam, causal, 0.8, 1e-5, pre_norm)
+        for name, g, w in zip(("dq1", "dq2", "dk1", "dk2", "dv", "dlam"), got, want):
+            np.testing.assert_allclose(g, w, rtol=1e-9, atol=1e-11,
+                                       err_msg=f"{name} nq={nq} causal={causal} pre_norm={pre_norm}")
+
+
+def test_backward_matches_autograd_of_library_forward():
+    check_against_autograd(obw)
+
+
+@pytest.mark.parametrize("causal,pre_norm", [(True, False), (False, False), (True, True)])
+def test_backward_matches_finite_differences_of_c_oracle(causal, pre_norm):
+    nq, d, dv, lam = 11, 5, 7, 0.6
+    c = _case(nq, d, dv, 40)
+
+    def loss(x, lam_):
+        out = oracle.head_rows(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], None, causal=causal,
+                               lam=lam_, lambda_init=0.8, eps=1e-5, pre_norm=pre_norm)
+        return float((out * c["dout"]).sum())
+
+    grads = obw.head_backward(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], lam, c["dout"],
+                              causal=causal, pre_norm=pre_norm)
+    rng = np.random.default_rng(41)
+    h = 1e-6
+    for i, name in enumerate(("q1", "q2", "k1", "k2", "v")):
+        u = rng.standard_normal(c[name].shape)
+        xp = dict(c); xp[name] = c[name] + h * u
+        xm = dict(c); xm[name] = c[name] - h * u
+        fd = (loss(xp, lam) - loss(xm, lam)) / (2 * h)
+        an = float((grads[i] * u).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    fd = (loss(c, lam + h) - loss(c, lam - h)) / (2 * h)
+    assert abs(fd - grads[5]) <= 1e-6 * max(1.0, abs(grads[5])), ("lambda", fd, grads[5])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_lse_reproduces_standard_attention(causal):
+    q, k, v = _rand((13, 8), 50), _rand((13, 8), 51), _rand((13, 5), 52)
+    lse = obw.head_lse(q, k, causal=causal)
+    s = (q @ k.T) / np.sqrt(8)
+    if causal:
+        s = np.where(np.tril(np.ones((13, 13))) > 0, s, -np.inf)
+    w = np.exp(s - lse[:, None])
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-13)
+    t = [torch.tensor(x)[None] for x in (q, k, v)]
+    want = F.scaled_dot_product_attention(*t, is_causal=causal)[0].numpy()
+    np.testing.assert_allclose(w @ v, want, rtol=1e-12, atol=1e-13)
+
+
+def test_lambda_zero_leaves_map_two_without_gradient():
+    c = _case(10, 4, 6, 60)
+    g = obw.head_backward(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], 0.0, c["dout"], causal=True)
+    assert np.all(g[1] == 0) and np.all(g[3] == 0)
+
+
+def test_batch_wrapper_sums_dlambda_over_batch():
+    rng = np.random.default_rng(70)
+    B, H, N, d, dv = 2, 3, 6, 4, 5
+    x = {k: rng.standard_normal((B, H, N, dv if k in ("v", "dout") else d))
+         for k in ("q1", "q2", "k1", "k2", "v", "dout")}
+    lam = np.array([0.2, 0.5, 0.9])
+    r = obw.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], lam, x["dout"], causal=True)
+    for h in range(H):
+        tot = sum(obw.head_backward(x["q1"][b, h], x["q2"][b, h], x["k1"][b, h], x["k2"][b, h],
+                                    x["v"][b, h], lam[h], x["dout"][b, h], causal=True)[5]
+                  for b in range(B))
+        assert r[5][h] == pytest.approx(tot, rel=1e-14)
+
+
+MUTANTS = [
+    ("dv = a1.T @ dD - lam * (a2.T @ dD)", "dv = a1.T @ dD + lam * (a2.T @ dD)"),
+    ("da2 = -lam * da1", "da2 = lam * da1"),
+    ("- xhat * (g * xhat).mean(axis=1, keepdims=True)) / sigma",
+     "+ xhat * (g * xhat).mean(axis=1, keepdims=True)) / sigma"),
+    ("g = (1.0 - lambda_init) * dout", "g = dout"),
+    ("dq1, dq2 = tau * (ds1 @ k1), tau * (ds2 @ k2)", "dq1, dq2 = ds1 @ k1, tau * (ds2 @ k2)"),
+    ("dlam = -float((o2 * dD).sum())", "dlam = float((o2 * dD).sum())"),
+    ("ds1 = a1 * (da1 - (a1 * da1).sum(axis=1, keepdims=True))", "ds1 = a1 * da1"),
+    ("dk1, dk2 = tau * (ds1.T @ q1), tau * (ds2.T @ q2)",
+     "dk1, dk2 = tau * (ds1.T @ q2), tau * (ds2.T @ q1)"),
+    ("g - g.mean(axis=1, keepdims=True)", "g"),
+    ("o1, o2 = a1 @ v, a2 @ v", "o1, o2 = a1 @ v, a1 @ v"),
+]
+
+
+@pytest.mark.parametrize("old,new", MUTANTS, ids=[str(i) for i in range(len(MUTANTS))])
+def test_planted_backward_mistake_is_caught(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("mutant_backward")
+    exec(compile(src.replace(old, new), "mutant_backward", "exec"), mod.__dict__)
+    with pytest.raises(AssertionError):
+        check_against_autograd(mod)
