@@ -97,6 +97,51 @@ int diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
                  void* out, const diffattn_dims* dims, void* stream);
 
 /*
+ * Training forward: diffattn_fwd plus what diffattn_bwd needs, for bf16 with
+ * (head_dim, v_dim) = (32, 64) or (64, 128) (else DIFFATTN_ERR_UNSUPPORTED).
+ * The backward differentiates the same operator: lambda is a learnable scalar
+ * (iloveeagents.com, "Mathematical Formula") and the GroupNorm of step 4 on
+ * llmbytes.dev ("How Differential Attention Cancels Common-Mode Noise") is
+ * there for stable gradients.
+ *   out as diffattn_fwd (same flags);
+ *   d_save [B][H][seq_q][dv] fp32: D = O1/l1 - lambda O2/l2 before the
+ *     GroupNorm;
+ *   lse [2][B][H][seq_q] fp32: natural-log log-sum-exp of each row of the
+ *     scaled scores, map 1 then map 2.
+ * All pointers device memory, 16-byte aligned, owned by the caller.
+ * Allocates nothing.  Returns a DIFFATTN_* status.
+ */
+int diffattn_fwd_train(const void* q1, const void* q2, const void* k1, const void* k2,
+                       const void* v, const float* lambda, float lambda_init, int causal,
+                       void* out, float* d_save, float* lse, const diffattn_dims* dims,
+                       void* stream);
+
+/*
+ * Workspace bytes diffattn_bwd needs (dD in bf16 and two fp32 row terms per
+ * query row); 0 when the sizes are invalid or unsupported.
+ */
+size_t diffattn_bwd_workspace_size(const diffattn_dims* dims);
+
+/*
+ * Backward: gradients of sum(dout * out) with out as written by
+ * diffattn_fwd_train with the same arguments (the flags, PRE_NORM included,
+ * must match), from its d_save and lse.
+ *   dout [B][H][seq_q][dv] bf16;
+ *   dq1, dq2 [B][H][seq_q][d], dk1, dk2 [B][H][seq_k][d], dv [B][H][seq_k][dv]
+ *     bf16 (fp32 accumulation, one rounding);
+ *   dlambda [H] fp32: summed over the batch and the query rows;
+ *   workspace: >= diffattn_bwd_workspace_size(dims) bytes, 16-byte aligned,
+ *     contents on entry ignored (DIFFATTN_ERR_WORKSPACE if too small).
+ * Same support matrix as diffattn_fwd_train.  Deterministic: no atomics.
+ * Allocates nothing.  Returns a DIFFATTN_* status.
+ */
+int diffattn_bwd(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                 const float* lambda, float lambda_init, int causal, const void* dout,
+                 const float* d_save, const float* lse, void* dq1, void* dq2, void* dk1,
+                 void* dk2, void* dv, float* dlambda, void* workspace, size_t workspace_bytes,
+                 const diffattn_dims* dims, void* stream);
+
+/*
  * Decode: one new query token per (b, h) against a KV cache.  Every cached
  * position of the sequence is visible (the cache already holds the current
  * token), so no mask applies.

@@ -54,6 +54,19 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=1, keepdims=True)
 
 
+def _norm_backward(D, dout, lambda_init: float, eps: float, pre_norm: bool) -> np.ndarray:
+    """dD from dy through y = (1 - lambda_init) (D - mu) / sigma, row-wise
+    (dD = dy when the output is D itself)."""
+    if pre_norm:
+        return dout
+    mu = D.mean(axis=1, keepdims=True)
+    sigma = np.sqrt(((D - mu) ** 2).mean(axis=1, keepdims=True) + eps)
+    xhat = (D - mu) / sigma
+    g = (1.0 - lambda_init) * dout
+    return (g - g.mean(axis=1, keepdims=True)
+            - xhat * (g * xhat).mean(axis=1, keepdims=True)) / sigma
+
+
 def head_lse(q, k, *, causal: bool) -> np.ndarray:
     """log(sum_j exp(S_ij)) of each row of one map's scores, fp64 [Nq]."""
     s = _scores(_f64(q), _f64(k), causal)
@@ -72,15 +85,7 @@ def head_backward(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
     a2 = _softmax_rows(_scores(q2, k2, causal))
     o1, o2 = a1 @ v, a2 @ v
     D = o1 - lam * o2
-    if pre_norm:
-        dD = dout
-    else:
-        mu = D.mean(axis=1, keepdims=True)
-        sigma = np.sqrt(((D - mu) ** 2).mean(axis=1, keepdims=True) + eps)
-        xhat = (D - mu) / sigma
-        g = (1.0 - lambda_init) * dout
-        dD = (g - g.mean(axis=1, keepdims=True)
-              - xhat * (g * xhat).mean(axis=1, keepdims=True)) / sigma
+    dD = _norm_backward(D, dout, lambda_init, eps, pre_norm)
     dv = a1.T @ dD - lam * (a2.T @ dD)
     da1 = dD @ v.T
     da2 = -lam * da1
@@ -90,6 +95,18 @@ def head_backward(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
     dk1, dk2 = tau * (ds1.T @ q1), tau * (ds2.T @ q2)
     dlam = -float((o2 * dD).sum())
     return dq1, dq2, dk1, dk2, dv, dlam
+
+
+def head_dlambda_terms(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
+                       lambda_init: float = 0.8, eps: float = 1e-5, pre_norm: bool = False):
+    """Per query row of one head: the row's share -O_2 . dD of dlambda and the
+    sum over channels of |O_2 dD| (the size of the terms that cancel in it)."""
+    q1, q2, k1, k2, v, dout = (_f64(t) for t in (q1, q2, k1, k2, v, dout))
+    a1 = _softmax_rows(_scores(q1, k1, causal))
+    a2 = _softmax_rows(_scores(q2, k2, causal))
+    o2 = a2 @ v
+    dD = _norm_backward(a1 @ v - lam * o2, dout, lambda_init, eps, pre_norm)
+    return -(o2 * dD).sum(axis=1), np.abs(o2 * dD).sum(axis=1)
 
 
 def backward(q1, q2, k1, k2, v, lam, dout, *, causal: bool, lambda_init: float = 0.8,

@@ -1,0 +1,184 @@
+"""GPU parity of the training pair (diffattn_fwd_train, diffattn_bwd) against
+the fp64 oracle (oracle/backward.py and the forward oracle), through the C ABI.
+
+Tolerances, from the arithmetic (bf16 operands, fp32 accumulation):
+* out: identical to diffattn_fwd (same kernel, same order of operations);
+* D (fp32 save): the forward's bf16 bound, 1.5e-2 + 2e-2 |oracle|;
+* log-sum-exp: 4e-3 absolute -- the row sum l is formed over probabilities
+  rounded to bf16 (2^-9 relative each), so log l is off by at most ~2^-9;
+* dQ, dK, dV: each element within 0.12 rms + 0.03 |oracle| + 1e-3, rms taken
+  over that gradient tensor (the 1e-3 floor, about 1% of these gradients'
+  rms, covers gradients that vanish exactly, e.g. dQ of a row that sees one
+  key).  Every gradient is a sum of products one of whose
+  factors (P, dS or dD) was rounded to bf16, and is itself stored in bf16; the
+  observed worst element is ~6% of the rms, a wrong sign, index or missing
+  term gives errors of the order of the rms itself;
+* dlambda: 3e-2 relative (a sum over all rows of fp32 row terms).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_diffattn_amd as da
+import workloads
+from oracle import backward as obw
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq1", "dq2", "dk1", "dk2", "dv")
+
+
+def _all_heads(x):
+    B, H = x["q1"].shape[:2]
+    return [(b, h) for b in range(B) for h in range(H)]
+
+
+def _inputs(B, H, n, d, dv, causal, seed, dist="normal"):
+    w = workloads.Workload("bwd", "prefill", B=B, H=H, nq=n, nk=n, d=d, dv=dv, dtype="bf16",
+                           causal=causal, dist=dist, lam=("uniform", 0.2, 0.9), seed=seed)
+    x = workloads.make_prefill(w)
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn((B, H, n, dv), generator=g, dtype=torch.float64).to(torch.bfloat16)
+    return w, x, dout
+
+
+def _gpu(x, dout, causal, pre_norm):
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    out, d_save, lse = da.fwd_train(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"],
+                                    causal=causal, pre_norm=pre_norm)
+    grads = da.bwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"], dout.cuda(), d_save,
+                   lse, causal=causal, pre_norm=pre_norm)
+    plain = da.fwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"], causal=causal,
+                   pre_norm=pre_norm)
+    torch.cuda.synchronize()
+    return out, d_save, lse, grads, plain
+
+
+def _check_grad(name, got, ref):
+    got = got.detach().double().cpu().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    rms = float(np.sqrt((ref ** 2).mean()))
+    err = np.abs(got - ref)
+    bound = 0.12 * rms + 0.03 * np.abs(ref) + 1e-3
+    i = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert np.all(err <= bound), (f"{name}: element {i} gpu {got[i]:.5f} oracle {ref[i]:.5f} "
+                                  f"(rms {rms:.4f}, max err {err.max():.4f})")
+
+
+def _dlam_noise(x, dout, causal, pre_norm, heads_b):
+    """Per head: sqrt(sum over rows of (sum_c |O_2 dD|)^2), the size of the
+    terms whose bf16 rounding (dD enters the kernels in bf16) sets dlambda's
+    error floor."""
+    lam = x["lam"].double().numpy()
+    out = {}
+    for (b, h) in heads_b:
+        _, a = obw.head_dlambda_terms(x["q1"][b, h], x["q2"][b, h], x["k1"][b, h], x["k2"][b, h],
+                                      x["v"][b, h], float(lam[h]), dout[b, h], causal=causal,
+                                      pre_norm=pre_norm)
+        out[h] = out.get(h, 0.0) + float((a ** 2).sum())
+    return {h: np.sqrt(v) for h, v in out.items()}
+
+
+def _check_dlam(got, ref, noise):
+    """dlambda sums per-row terms of both signs that can cancel (for one
+    visible key it is exactly 0: dD is orthogonal to D), so beside 3e-2
+    relative it gets 2^-6 of the terms' size (about 4x bf16's 2^-8 per row,
+    summed as a random walk) as an absolute floor."""
+    got = got.detach().double().cpu().numpy()
+    floor = np.array([noise[h] for h in sorted(noise)]) * 2.0 ** -6
+    assert np.all(np.abs(got - ref) <= 3e-2 * np.abs(ref) + floor), (got, ref, floor)
+
+
+@pytest.mark.parametrize("d,dv", [(32, 64), (64, 128)], ids=["d32", "d64"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("n", [1, 7, 64, 129, 300])
+def test_backward_small(d, dv, causal, n):
+    w, x, dout = _inputs(2, 3, n, d, dv, causal, seed=500 + n + d)
+    out, d_save, lse, grads, plain = _gpu(x, dout, causal, False)
+    assert torch.equal(out, plain), "training forward output differs from the forward"
+    D = oracle.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=causal,
+                   pre_norm=True)
+    Dg = d_save.double().cpu().numpy()
+    assert np.all(np.abs(Dg - D) <= 1.5e-2 + 2e-2 * np.abs(D)), "saved D"
+    for k, (q, kk) in enumerate((("q1", "k1"), ("q2", "k2"))):
+        ref_lse = obw.lse(x[q], x[kk], causal=causal)
+        assert np.abs(lse[k].double().cpu().numpy() - ref_lse).max() <= 4e-3, f"lse of map {k + 1}"
+    ref = obw.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], dout, causal=causal)
+    for name, gg, rr in zip(NAMES, grads[:5], ref[:5]):
+        _check_grad(f"{name} d{d} n{n} causal={causal}", gg, rr)
+    _check_dlam(grads[5], ref[5], _dlam_noise(x, dout, causal, False, _all_heads(x)))
+
+
+@pytest.mark.parametrize("d,dv,causal", [(64, 128, True), (32, 64, False)])
+def test_backward_pre_norm_output(d, dv, causal):
+    w, x, dout = _inputs(1, 2, 150, d, dv, causal, seed=77)
+    out, d_save, lse, grads, plain = _gpu(x, dout, causal, True)
+    assert torch.equal(out, plain)
+    ref = obw.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], dout, causal=causal,
+                       pre_norm=True)
+    for name, gg, rr in zip(NAMES, grads[:5], ref[:5]):
+        _check_grad(name, gg, rr)
+    _check_dlam(grads[5], ref[5], _dlam_noise(x, dout, causal, True, _all_heads(x)))
+
+
+def test_backward_rectangular_noncausal():
+    B, H, nq, nk, d, dv = 1, 2, 70, 200, 64, 128
+    w = workloads.Workload("bwd", "prefill", B=B, H=H, nq=nq, nk=nk, d=d, dv=dv, dtype="bf16",
+                           causal=False, lam=("uniform", 0.2, 0.9), seed=91)
+    x = workloads.make_prefill(w)
+    dout = torch.randn((B, H, nq, dv), generator=torch.Generator().manual_seed(92),
+                       dtype=torch.float64).to(torch.bfloat16)
+    out, d_save, lse, grads, plain = _gpu(x, dout, False, False)
+    ref = obw.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], dout, causal=False)
+    for name, gg, rr in zip(NAMES, grads[:5], ref[:5]):
+        _check_grad(name, gg, rr)
+    _check_dlam(grads[5], ref[5], _dlam_noise(x, dout, False, False, _all_heads(x)))
+
+
+def test_backward_deterministic():
+    w, x, dout = _inputs(1, 4, 300, 64, 128, True, seed=93)
+    a = _gpu(x, dout, True, False)[3]
+    b = _gpu(x, dout, True, False)[3]
+    for ga, gb in zip(a, b):
+        assert torch.equal(ga, gb)
+
+
+def test_backward_rejects_unsupported_and_small_workspace():
+    w, x, dout = _inputs(1, 1, 16, 128, 256, True, seed=94)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    with pytest.raises(ValueError):
+        da.fwd_train(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"], causal=True)
+    w, x, dout = _inputs(1, 2, 64, 64, 128, True, seed=95)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    out, d_save, lse = da.fwd_train(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"],
+                                    causal=True)
+    small = torch.empty((16,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(da.DiffAttnError):
+        da.bwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"], dout.cuda(), d_save, lse,
+               causal=True, workspace=small)
+
+
+def test_backward_headline_shape_sampled_heads():
+    """The headline prefill shape (B4 H16 N2048 d64 dv128, causal): the GPU
+    computes every head; three heads are checked in full, and dlambda of two
+    heads over the whole batch."""
+    w = workloads.get("causal_prefill_bf16")
+    x = workloads.make_prefill(w)
+    dout = torch.randn((w.B, w.H, w.nq, w.dv), generator=torch.Generator().manual_seed(96),
+                       dtype=torch.float64).to(torch.bfloat16)
+    out, d_save, lse, grads, plain = _gpu(x, dout, True, False)
+    grads = [g.cpu() for g in grads]
+    lam = x["lam"].double().numpy()
+    for (b, h) in [(0, 0), (1, 7), (3, 15)]:
+        r = obw.head_backward(x["q1"][b, h], x["q2"][b, h], x["k1"][b, h], x["k2"][b, h],
+                              x["v"][b, h], float(lam[h]), dout[b, h], causal=True)
+        for name, gg, rr in zip(NAMES, grads[:5], r[:5]):
+            _check_grad(f"{name} b{b} h{h}", gg[b, h], rr)
+    for h in (3, 12):
+        tot = sum(obw.head_backward(x["q1"][b, h], x["q2"][b, h], x["k1"][b, h], x["k2"][b, h],
+                                    x["v"][b, h], float(lam[h]), dout[b, h], causal=True)[5]
+                  for b in range(w.B))
+        noise = _dlam_noise(x, dout, True, False, [(b, h) for b in range(w.B)])
+        _check_dlam(grads[5][h:h + 1], np.array([tot]), noise)

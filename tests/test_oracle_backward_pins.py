@@ -128,11 +128,24 @@ def test_batch_wrapper_sums_dlambda_over_batch():
         assert r[5][h] == pytest.approx(tot, rel=1e-14)
 
 
+def test_dlambda_terms_sum_to_dlambda():
+    c = _case(14, 6, 9, 80)
+    for pre_norm in (False, True):
+        r, a = obw.head_dlambda_terms(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], 0.7, c["dout"],
+                                      causal=True, pre_norm=pre_norm)
+        full = obw.head_backward(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], 0.7, c["dout"],
+                                 causal=True, pre_norm=pre_norm)[5]
+        assert r.sum() == pytest.approx(full, rel=1e-12)
+        assert np.all(a >= np.abs(r))
+
+
 MUTANTS = [
     ("dv = a1.T @ dD - lam * (a2.T @ dD)", "dv = a1.T @ dD + lam * (a2.T @ dD)"),
     ("da2 = -lam * da1", "da2 = lam * da1"),
     ("- xhat * (g * xhat).mean(axis=1, keepdims=True)) / sigma",
      "+ xhat * (g * xhat).mean(axis=1, keepdims=True)) / sigma"),
+    ("sigma = np.sqrt(((D - mu) ** 2).mean(axis=1, keepdims=True) + eps)",
+     "sigma = np.sqrt(((D - mu) ** 2).mean(axis=1, keepdims=True)) + eps"),
     ("g = (1.0 - lambda_init) * dout", "g = dout"),
     ("dq1, dq2 = tau * (ds1 @ k1), tau * (ds2 @ k2)", "dq1, dq2 = ds1 @ k1, tau * (ds2 @ k2)"),
     ("dlam = -float((o2 * dD).sum())", "dlam = float((o2 * dD).sum())"),

@@ -84,6 +84,13 @@ def lib():
         L.diffattn_decode_default_splits.argtypes = [DP]
         L.diffattn_decode_workspace_size.restype = ctypes.c_size_t
         L.diffattn_decode_workspace_size.argtypes = [DP, ctypes.c_int32]
+        L.diffattn_fwd_train.restype = I
+        L.diffattn_fwd_train.argtypes = [P, P, P, P, P, P, F, I, P, P, P, DP, P]
+        L.diffattn_bwd_workspace_size.restype = ctypes.c_size_t
+        L.diffattn_bwd_workspace_size.argtypes = [DP]
+        L.diffattn_bwd.restype = I
+        L.diffattn_bwd.argtypes = [P, P, P, P, P, P, F, I, P, P, P, P, P, P, P, P, P, P,
+                                   ctypes.c_size_t, DP, P]
         _lib = L
     return _lib
 
@@ -168,6 +175,83 @@ def fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
                             out.data_ptr(), ctypes.byref(dims), _stream_ptr(q1.device))
     _check(st)
     return out
+
+
+def _check_inputs(q1, q2, k1, k2, v):
+    ts = (q1, q2, k1, k2, v)
+    _require(all(t.is_cuda for t in ts), "inputs must be GPU tensors")
+    _require(all(t.device == q1.device for t in ts), "inputs must share one device")
+    _require(all(t.dtype == q1.dtype for t in ts), "inputs must share one dtype")
+    _require(all(t.dim() == 4 for t in ts), "inputs must be [B,H,N,dim]")
+    _require(all(t.is_contiguous() for t in ts), "inputs must be contiguous")
+    B, H, Nq, d = q1.shape
+    Nk, dv = k1.shape[2], v.shape[3]
+    _require(q2.shape == (B, H, Nq, d), "q2 shape must equal q1 shape")
+    _require(k1.shape == (B, H, Nk, d) and k2.shape == (B, H, Nk, d), "k1/k2 shape mismatch")
+    _require(v.shape == (B, H, Nk, dv), "v shape mismatch")
+    return B, H, Nq, Nk, d, dv
+
+
+def fwd_train(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
+              v: torch.Tensor, lam: Union[float, Sequence[float], torch.Tensor],
+              lambda_init: float = 0.8, causal: bool = True, eps: float = 1e-5,
+              pre_norm: bool = False):
+    """Training forward (bf16, d = 32 or 64): returns (out, d_save, lse) with
+    d_save = D [B,H,Nq,dv] fp32 and lse [2,B,H,Nq] fp32 (natural-log
+    log-sum-exp of each map's score rows), the inputs of ``bwd``."""
+    B, H, Nq, Nk, d, dv = _check_inputs(q1, q2, k1, k2, v)
+    dev = q1.device
+    out = torch.empty((B, H, Nq, dv), dtype=q1.dtype, device=dev)
+    d_save = torch.empty((B, H, Nq, dv), dtype=torch.float32, device=dev)
+    lse = torch.empty((2, B, H, Nq), dtype=torch.float32, device=dev)
+    lam_t = _lam_tensor(lam, H, dev)
+    dims = Dims(B, H, Nq, Nk, d, dv, _dtype_code(q1), float(eps),
+                FLAG_PRE_NORM if pre_norm else 0)
+    st = lib().diffattn_fwd_train(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
+                                  v.data_ptr(), lam_t.data_ptr(), float(lambda_init),
+                                  int(bool(causal)), out.data_ptr(), d_save.data_ptr(),
+                                  lse.data_ptr(), ctypes.byref(dims), _stream_ptr(dev))
+    _check(st)
+    return out, d_save, lse
+
+
+def bwd_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, dv: int) -> int:
+    """Bytes of device workspace ``bwd`` needs (bf16 sizes)."""
+    dims = Dims(B, H, Nq, Nk, d, dv, BF16, 1e-5, 0)
+    return int(lib().diffattn_bwd_workspace_size(ctypes.byref(dims)))
+
+
+def bwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
+        v: torch.Tensor, lam: Union[float, Sequence[float], torch.Tensor], dout: torch.Tensor,
+        d_save: torch.Tensor, lse: torch.Tensor, lambda_init: float = 0.8, causal: bool = True,
+        eps: float = 1e-5, pre_norm: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Backward of ``fwd_train`` (same arguments): gradients of sum(dout * out).
+    Returns (dq1, dq2, dk1, dk2, dv) in the input dtype and dlambda [H] fp32
+    (summed over batch and rows; sum it for a scalar lambda)."""
+    B, H, Nq, Nk, d, dv = _check_inputs(q1, q2, k1, k2, v)
+    dev = q1.device
+    _require(dout.shape == (B, H, Nq, dv) and dout.dtype == q1.dtype and dout.is_contiguous()
+             and dout.device == dev, "dout must be a contiguous [B,H,Nq,dv] tensor like out")
+    _require(d_save.shape == (B, H, Nq, dv) and d_save.dtype == torch.float32
+             and d_save.is_contiguous(), "d_save must be the fp32 [B,H,Nq,dv] from fwd_train")
+    _require(lse.shape == (2, B, H, Nq) and lse.dtype == torch.float32 and lse.is_contiguous(),
+             "lse must be the fp32 [2,B,H,Nq] from fwd_train")
+    grads = [torch.empty_like(t) for t in (q1, q2, k1, k2, v)]
+    dlam = torch.empty((H,), dtype=torch.float32, device=dev)
+    dims = Dims(B, H, Nq, Nk, d, dv, _dtype_code(q1), float(eps),
+                FLAG_PRE_NORM if pre_norm else 0)
+    need = int(lib().diffattn_bwd_workspace_size(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    lam_t = _lam_tensor(lam, H, dev)
+    st = lib().diffattn_bwd(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
+                            v.data_ptr(), lam_t.data_ptr(), float(lambda_init), int(bool(causal)),
+                            dout.data_ptr(), d_save.data_ptr(), lse.data_ptr(),
+                            *[g.data_ptr() for g in grads], dlam.data_ptr(), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), ctypes.byref(dims),
+                            _stream_ptr(dev))
+    _check(st)
+    return (*grads, dlam)
 
 
 def _decode_dims(B, H, L, d, dv, dtype_code, eps, pre_norm) -> Dims:

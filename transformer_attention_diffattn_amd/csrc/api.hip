@@ -142,10 +142,112 @@ int diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
     a.eps = dims->eps;
     a.scale_log2 = scale_log2(dims->head_dim);
     a.flags = dims->flags;
+    a.d_save = nullptr;
+    a.lse = nullptr;
     hipStream_t s = (hipStream_t)stream;
     const hipError_t e = dims->dtype == DIFFATTN_BF16
                              ? launch_prefill_bf16(a, dims->head_dim, dims->v_dim, causal != 0, s)
                              : launch_prefill_f32(a, dims->head_dim, dims->v_dim, causal != 0, s);
+    return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
+}
+
+// The training pair (forward that saves D and the log-sum-exp, backward):
+// bf16 with (d, dv) = (32, 64) or (64, 128).
+static int check_train_dims(const diffattn_dims* dims, int causal) {
+    int st = check_dims(dims);
+    if (st != DIFFATTN_OK) return st;
+    if (dims->dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+    if (!((dims->head_dim == 32 && dims->v_dim == 64) || (dims->head_dim == 64 && dims->v_dim == 128)))
+        return DIFFATTN_ERR_UNSUPPORTED;
+    if (causal && dims->seq_q != dims->seq_k) return DIFFATTN_ERR_UNSUPPORTED;
+    return DIFFATTN_OK;
+}
+
+int diffattn_fwd_train(const void* q1, const void* q2, const void* k1, const void* k2,
+                       const void* v, const float* lambda, float lambda_init, int causal,
+                       void* out, float* d_save, float* lse, const diffattn_dims* dims,
+                       void* stream) {
+    int st = check_train_dims(dims, causal);
+    if (st != DIFFATTN_OK) return st;
+    const void* ptrs[] = {q1, q2, k1, k2, v, lambda, out, d_save, lse};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return DIFFATTN_ERR_INVALID;
+    if (!isfinite(lambda_init)) return DIFFATTN_ERR_INVALID;
+
+    PrefillArgs a;
+    a.q1 = q1;
+    a.q2 = q2;
+    a.k1 = k1;
+    a.k2 = k2;
+    a.v = v;
+    a.lam = lambda;
+    a.out = out;
+    a.B = dims->batch;
+    a.H = dims->heads;
+    a.Nq = dims->seq_q;
+    a.Nk = dims->seq_k;
+    a.lambda_init = lambda_init;
+    a.eps = dims->eps;
+    a.scale_log2 = scale_log2(dims->head_dim);
+    a.flags = dims->flags;
+    a.d_save = d_save;
+    a.lse = lse;
+    const hipError_t e = launch_prefill_bf16(a, dims->head_dim, dims->v_dim, causal != 0,
+                                             (hipStream_t)stream);
+    return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
+}
+
+size_t diffattn_bwd_workspace_size(const diffattn_dims* dims) {
+    if (check_train_dims(dims, 0) != DIFFATTN_OK) return 0;
+    return backward_workspace_bytes(dims->batch, dims->heads, dims->seq_q, dims->v_dim);
+}
+
+int diffattn_bwd(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
+                 const float* lambda, float lambda_init, int causal, const void* dout,
+                 const float* d_save, const float* lse, void* dq1, void* dq2, void* dk1,
+                 void* dk2, void* dv, float* dlambda, void* workspace, size_t workspace_bytes,
+                 const diffattn_dims* dims, void* stream) {
+    int st = check_train_dims(dims, causal);
+    if (st != DIFFATTN_OK) return st;
+    const void* ptrs[] = {q1, q2, k1, k2, v, lambda, dout, d_save, lse,
+                          dq1, dq2, dk1, dk2, dv, dlambda, workspace};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return DIFFATTN_ERR_INVALID;
+    if (!isfinite(lambda_init)) return DIFFATTN_ERR_INVALID;
+    const size_t need =
+        backward_workspace_bytes(dims->batch, dims->heads, dims->seq_q, dims->v_dim);
+    if (workspace_bytes < need) return DIFFATTN_ERR_WORKSPACE;
+
+    BackwardArgs a;
+    a.q1 = q1;
+    a.q2 = q2;
+    a.k1 = k1;
+    a.k2 = k2;
+    a.v = v;
+    a.lam = lambda;
+    a.dout = dout;
+    a.d_save = d_save;
+    a.lse = lse;
+    a.dq1 = dq1;
+    a.dq2 = dq2;
+    a.dk1 = dk1;
+    a.dk2 = dk2;
+    a.dv = dv;
+    a.dlam = dlambda;
+    a.dd = workspace;
+    a.delta = (float*)((char*)workspace +
+                       ((size_t)dims->batch * dims->heads * dims->seq_q * dims->v_dim * 2 + 255) /
+                           256 * 256);
+    a.B = dims->batch;
+    a.H = dims->heads;
+    a.Nq = dims->seq_q;
+    a.Nk = dims->seq_k;
+    a.lambda_init = lambda_init;
+    a.eps = dims->eps;
+    a.scale_log2 = scale_log2(dims->head_dim);
+    a.flags = dims->flags;
+    const hipError_t e = launch_backward_bf16(a, dims->head_dim, dims->v_dim, causal != 0,
+                                              (hipStream_t)stream);
     return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
 }
 

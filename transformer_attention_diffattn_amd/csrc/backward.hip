@@ -1,0 +1,462 @@
+// Backward of the fused Differential Attention operator for bf16 inputs on
+// gfx950, head_dim 32 or 64 (v_dim 64 or 128).
+//
+// The pages treat the operator as trained: lambda is learnable
+// (iloveeagents.com, "Mathematical Formula") and the per-head GroupNorm with
+// the (1 - lambda_init) scale of step 4 on llmbytes.dev ("How Differential
+// Attention Cancels Common-Mode Noise") keeps gradients stable.  This is the
+// chain rule through that forward, in the forward's notation (tau = 1/sqrt(d)):
+//
+//   dD   = GroupNorm backward of dy (or dy itself for a pre-norm output);
+//   dP   = dD V^T                       (shared by both maps: dA1 = dP,
+//                                        dA2 = -lambda dP);
+//   delta_k = rowsum(A_k * dP);
+//   dS_1 = A_1 (dP - delta_1),  dS_2 = -lambda A_2 (dP - delta_2);
+//   dQ_k = tau dS_k K_k,  dK_k = tau dS_k^T Q_k,  dV = (A_1 - lambda A_2)^T dD;
+//   dlambda = -sum(O_2 . dD) = -sum_rows delta_2.
+//
+// A_k is recomputed from the scores and the per-row log-sum-exp that the
+// training forward saved, so no N x N map is ever stored.  Four kernels, in
+// stream order:
+//   prep   one wave per row: dD from the saved D and dy, in bf16 for the MFMAs;
+//   dq     a workgroup per 64 query rows (wave = 32 rows of one map), looping
+//          over key tiles; dQ_k = tau (X_k - delta_k Y_k) with X_k = (A_k * dP)
+//          K_k and Y_k = A_k K_k, so delta_k comes out of the same sweep;
+//          writes dQ and delta_k;
+//   dkdv   a workgroup per 128 keys (wave = 32 keys, both maps), looping over
+//          query tiles; accumulates dV^T and dK_k^T;
+//   dlam   one workgroup per head: dlambda = -sum delta_2 (fixed order).
+//
+// MFMA v_mfma_f32_32x32x16_bf16 throughout (lane l, lh = l / 32, l32 = l % 32:
+// A row l32 / B column l32 hold k-slots 8 lh .. 8 lh + 7; accumulator register
+// r is row 8 (r/4) + 4 lh + r%4, column l32).  A product whose output rows feed
+// the next product's k dimension loads its A rows in swap23 order, which makes
+// accumulator registers 8c .. 8c+7 exactly the k-slots of 16-row step c; the
+// other operands are either rows read 16 bytes at a time or columns read with
+// the transposing ds_read_b64_tr_b16.  Tiles sit in LDS row-major with rows
+// padded by 16 bytes.
+
+#include "internal.h"
+
+#include <math.h>
+
+namespace diffattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kBwdThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int swap23(int r) {
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes of row `row` at column k0 + 8 lh (row-major tile, `stride` elements)
+__device__ __forceinline__ bf16x8 rd_row(const uint16_t* t, int stride, int row, int k0, int lh) {
+    return *(const bf16x8*)(t + row * stride + k0 + 8 * lh);
+}
+
+// Column cb + l32 of rows k0 + 8 lh .. k0 + 8 lh + 7: two transposing reads.
+// Within a 16-lane group, lane 4e + r addresses row e at column base + 4r and
+// receives column base + (lane % 16) of the 4 rows.
+__device__ __forceinline__ bf16x8 rd_col(const uint16_t* t, int stride, int k0, int cb, int lane) {
+    const int g = lane >> 4, e = (lane & 15) >> 2, r = lane & 3;
+    const uint16_t* p = t + (k0 + 8 * (g >> 1) + e) * stride + cb + 16 * (g & 1) + 4 * r;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(p + 4 * stride));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// registers 8c .. 8c+7 of an accumulator, rounded to bf16 (one B or A operand)
+__device__ __forceinline__ void pack(const float (&x)[16], bf16x8 (&o)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[c][j] = (__bf16)x[8 * c + j];
+}
+
+// rows [row0, row0 + rows) of a [n][W] bf16 tensor into a padded LDS tile;
+// rows at or past n are zero
+template <int W>
+__device__ __forceinline__ void stage_rows(uint16_t* t, const uint16_t* g, int64_t row0, int rows,
+                                           int64_t n) {
+    constexpr int kStride = W + 8;
+    constexpr int kCpr = W / 8;  // 16-byte chunks per row
+    for (int c = threadIdx.x; c < rows * kCpr; c += kBwdThreads) {
+        const int r = c / kCpr, ch = c % kCpr;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row0 + r < n) v = *(const uint4*)(g + (row0 + r) * W + 8 * ch);
+        *(uint4*)(t + r * kStride + 8 * ch) = v;
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// prep: dD for every row (one wave per row)
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BackwardArgs a) {
+    constexpr int kPer = DV / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+    const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+    if (row >= rows) return;
+    const float* drow = a.d_save + row * DV;
+    const __bf16* gy = (const __bf16*)a.dout + row * DV;
+    __bf16* out = (__bf16*)a.dd + row * DV;
+    float y[kPer], dd[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) y[i] = (float)gy[lane + 64 * i];
+    if (a.flags & 1u) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) dd[i] = y[i];
+    } else {
+        float x[kPer], s = 0.f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            x[i] = drow[lane + 64 * i];
+            s += x[i];
+        }
+        const float mu = wave_sum(s) * (1.f / DV);
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) q = fmaf(x[i] - mu, x[i] - mu, q);
+        const float inv = 1.f / sqrtf(wave_sum(q) * (1.f / DV) + a.eps);
+        const float c = 1.f - a.lambda_init;
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            x[i] = (x[i] - mu) * inv;  // xhat
+            y[i] *= c;                 // g
+            sg += y[i];
+            sgx = fmaf(y[i], x[i], sgx);
+        }
+        const float mg = wave_sum(sg) * (1.f / DV);
+        const float mgx = wave_sum(sgx) * (1.f / DV);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) dd[i] = (y[i] - mg - x[i] * mgx) * inv;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) out[lane + 64 * i] = (__bf16)dd[i];
+}
+
+// ---------------------------------------------------------------------------
+// dq: dQ_k and delta_k.  Workgroup = 64 query rows of one (b, h); wave w owns
+// rows 32 (w % 2) .. of map w / 2.
+// ---------------------------------------------------------------------------
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
+    constexpr int NKB = D / 16, NVB = DV / 16, NCB = D / 32;
+    constexpr int KS = D + 8, VS = DV + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][32 * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[32 * VS];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int qb = wave & 1, map = wave >> 1;
+    const int BH = a.B * a.H;
+    const int nqt = (a.Nq + 63) / 64;
+    const int t = blockIdx.x / BH;  // longest causal tiles first
+    const int bh = blockIdx.x - t * BH;
+    const int qt = CAUSAL ? nqt - 1 - t : t;
+    const int h = bh % a.H;
+    const int qrow = qt * 64 + qb * 32 + l32;
+    const bool qok = qrow < a.Nq;
+
+    const uint16_t* gq = (const uint16_t*)(map ? a.q2 : a.q1) + (size_t)bh * a.Nq * D;
+    const uint16_t* gk1 = (const uint16_t*)a.k1 + (size_t)bh * a.Nk * D;
+    const uint16_t* gk2 = (const uint16_t*)a.k2 + (size_t)bh * a.Nk * D;
+    const uint16_t* gv = (const uint16_t*)a.v + (size_t)bh * a.Nk * DV;
+    const uint16_t* gdd = (const uint16_t*)a.dd + (size_t)bh * a.Nq * DV;
+
+    // B operands of this lane's query (column l32): Q_k^T over d, dD^T over dv
+    bf16x8 qf[NKB], df[NVB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+        qf[kb] = qok ? *(const bf16x8*)(gq + (size_t)qrow * D + 16 * kb + 8 * lh) : bf16x8{};
+#pragma unroll
+    for (int c = 0; c < NVB; ++c)
+        df[c] = qok ? *(const bf16x8*)(gdd + (size_t)qrow * DV + 16 * c + 8 * lh) : bf16x8{};
+    const float lse2 =
+        qok ? a.lse[((size_t)map * BH + bh) * a.Nq + qrow] * kLog2e : 0.f;
+    const float sl2 = a.scale_log2;
+
+    f32x16 xt[NCB], yt[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) xt[cb] = yt[cb] = f32x16{};
+    float dsum = 0.f;
+
+    const int nkt_all = (a.Nk + 31) / 32;
+    const int nkt = CAUSAL ? min(nkt_all, (qt * 64 + 64 + 31) / 32) : nkt_all;
+    for (int kt = 0; kt < nkt; ++kt) {
+        stage_rows<D>(sk[0], gk1, (int64_t)kt * 32, 32, a.Nk);
+        stage_rows<D>(sk[1], gk2, (int64_t)kt * 32, 32, a.Nk);
+        stage_rows<DV>(sv, gv, (int64_t)kt * 32, 32, a.Nk);
+        __syncthreads();
+        const uint16_t* kt_ = sk[map];
+        // S^T = K Q^T and dP^T = V dD^T, key rows in swap23 order
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const int kr = swap23(l32);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s = mfma(rd_row(kt_, KS, kr, 16 * kb, lh), qf[kb], s);
+#pragma unroll
+        for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sv, VS, kr, 16 * c, lh), df[c], dp);
+        float p[16], w[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kt * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+            const bool ok = qok && key < a.Nk && (!CAUSAL || key <= qrow);
+            p[r] = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2)) : 0.f;
+            w[r] = p[r] * dp[r];
+            dsum += w[r];
+        }
+        bf16x8 pp[2], pw[2];
+        pack(p, pp);
+        pack(w, pw);
+        // X^T += K^T (A*dP)^T,  Y^T += K^T A^T
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 kc = rd_col(kt_, KS, 16 * kk, 32 * cb, lane);
+                xt[cb] = mfma(kc, pw[kk], xt[cb]);
+                yt[cb] = mfma(kc, pp[kk], yt[cb]);
+            }
+        }
+        __syncthreads();
+    }
+
+    const float delta = dsum + __shfl_xor(dsum, 32);
+    if (!qok) return;
+    const float tau = 1.f / sqrtf((float)D);
+    const float sc = map ? -a.lam[h] * tau : tau;
+    __bf16* gout = (__bf16*)(map ? a.dq2 : a.dq1) + ((size_t)bh * a.Nq + qrow) * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = (__bf16)(sc * (xt[cb][4 * g + e] - delta * yt[cb][4 * g + e]));
+            *(bf16x4*)(gout + 32 * cb + 8 * g + 4 * lh) = o;
+        }
+    }
+    if (lh == 0) a.delta[((size_t)map * BH + bh) * a.Nq + qrow] = delta;
+}
+
+// ---------------------------------------------------------------------------
+// dkdv: dK_1, dK_2 and dV.  Workgroup = 128 keys of one (b, h); wave w owns
+// keys 32 w .. 32 w + 31 and both maps.
+// ---------------------------------------------------------------------------
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BackwardArgs a) {
+    constexpr int NKB = D / 16, NVB = DV / 16, NCB = D / 32, NDB = DV / 32;
+    constexpr int KS = D + 8, VS = DV + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sq[2][32 * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t sd[32 * VS];
+    __shared__ __attribute__((aligned(16))) float srow[4][32];  // lse1, lse2 (log2), delta1, delta2
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int BH = a.B * a.H;
+    // key tile kt = blockIdx / BH: under the causal mask the first key tiles
+    // see the most queries, so the longest workgroups start first
+    const int kt = blockIdx.x / BH;
+    const int bh = blockIdx.x - kt * BH;
+    const int h = bh % a.H;
+    const int key = kt * 128 + wave * 32 + l32;
+    const bool kok = key < a.Nk;
+
+    const uint16_t* gk1 = (const uint16_t*)a.k1 + (size_t)bh * a.Nk * D;
+    const uint16_t* gk2 = (const uint16_t*)a.k2 + (size_t)bh * a.Nk * D;
+    const uint16_t* gv = (const uint16_t*)a.v + (size_t)bh * a.Nk * DV;
+    const uint16_t* gq1 = (const uint16_t*)a.q1 + (size_t)bh * a.Nq * D;
+    const uint16_t* gq2 = (const uint16_t*)a.q2 + (size_t)bh * a.Nq * D;
+    const uint16_t* gdd = (const uint16_t*)a.dd + (size_t)bh * a.Nq * DV;
+
+    // B operands of this lane's key (column l32): K_k^T over d, V^T over dv
+    bf16x8 k1f[NKB], k2f[NKB], vf[NVB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        k1f[kb] = kok ? *(const bf16x8*)(gk1 + (size_t)key * D + 16 * kb + 8 * lh) : bf16x8{};
+        k2f[kb] = kok ? *(const bf16x8*)(gk2 + (size_t)key * D + 16 * kb + 8 * lh) : bf16x8{};
+    }
+#pragma unroll
+    for (int c = 0; c < NVB; ++c)
+        vf[c] = kok ? *(const bf16x8*)(gv + (size_t)key * DV + 16 * c + 8 * lh) : bf16x8{};
+    const float sl2 = a.scale_log2;
+    const float lam = a.lam[h];
+
+    f32x16 dvt[NDB], dk1t[NCB], dk2t[NCB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dvt[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) dk1t[i] = dk2t[i] = f32x16{};
+
+    const int nqt = (a.Nq + 31) / 32;
+    const int qt0 = CAUSAL ? (kt * 128) / 32 : 0;
+    const float* lse1 = a.lse + (size_t)bh * a.Nq;
+    const float* lse2 = a.lse + ((size_t)BH + bh) * a.Nq;
+    const float* del1 = a.delta + (size_t)bh * a.Nq;
+    const float* del2 = a.delta + ((size_t)BH + bh) * a.Nq;
+    for (int qt = qt0; qt < nqt; ++qt) {
+        stage_rows<D>(sq[0], gq1, (int64_t)qt * 32, 32, a.Nq);
+        stage_rows<D>(sq[1], gq2, (int64_t)qt * 32, 32, a.Nq);
+        stage_rows<DV>(sd, gdd, (int64_t)qt * 32, 32, a.Nq);
+        if (threadIdx.x < 128) {
+            const int which = threadIdx.x >> 5, i = threadIdx.x & 31;
+            const int q = qt * 32 + i;
+            const float* src = which == 0 ? lse1 : which == 1 ? lse2 : which == 2 ? del1 : del2;
+            const float v = q < a.Nq ? src[q] : 0.f;
+            srow[which][i] = which < 2 ? v * kLog2e : v;
+        }
+        __syncthreads();
+        // S_k = Q_k K_k^T and dP = dD V^T, query rows in swap23 order
+        const int qr = swap23(l32);
+        f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s1 = mfma(rd_row(sq[0], KS, qr, 16 * kb, lh), k1f[kb], s1);
+            s2 = mfma(rd_row(sq[1], KS, qr, 16 * kb, lh), k2f[kb], s2);
+        }
+#pragma unroll
+        for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sd, VS, qr, 16 * c, lh), vf[c], dp);
+        float wd[16], d1[16], d2[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
+            const int q = qt * 32 + qi;
+            const bool ok = kok && q < a.Nq && (!CAUSAL || key <= q);
+            const float p1 = ok ? __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, -srow[0][qi])) : 0.f;
+            const float p2 = ok ? __builtin_amdgcn_exp2f(fmaf(s2[r], sl2, -srow[1][qi])) : 0.f;
+            wd[r] = p1 - lam * p2;
+            d1[r] = p1 * (dp[r] - srow[2][qi]);
+            d2[r] = -lam * p2 * (dp[r] - srow[3][qi]);
+        }
+        bf16x8 pwd[2], pd1[2], pd2[2];
+        pack(wd, pwd);
+        pack(d1, pd1);
+        pack(d2, pd2);
+        // dV^T += dD^T W,  dK_k^T += Q_k^T dS_k  (k = queries)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int cb = 0; cb < NDB; ++cb)
+                dvt[cb] = mfma(rd_col(sd, VS, 16 * kk, 32 * cb, lane), pwd[kk], dvt[cb]);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                dk1t[cb] = mfma(rd_col(sq[0], KS, 16 * kk, 32 * cb, lane), pd1[kk], dk1t[cb]);
+                dk2t[cb] = mfma(rd_col(sq[1], KS, 16 * kk, 32 * cb, lane), pd2[kk], dk2t[cb]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (!kok) return;
+    const float tau = 1.f / sqrtf((float)D);
+    __bf16* o1 = (__bf16*)a.dk1 + ((size_t)bh * a.Nk + key) * D;
+    __bf16* o2 = (__bf16*)a.dk2 + ((size_t)bh * a.Nk + key) * D;
+    __bf16* ov = (__bf16*)a.dv + ((size_t)bh * a.Nk + key) * DV;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            bf16x4 w1, w2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w1[e] = (__bf16)(tau * dk1t[cb][4 * g + e]);
+                w2[e] = (__bf16)(tau * dk2t[cb][4 * g + e]);
+            }
+            *(bf16x4*)(o1 + 32 * cb + 8 * g + 4 * lh) = w1;
+            *(bf16x4*)(o2 + 32 * cb + 8 * g + 4 * lh) = w2;
+        }
+#pragma unroll
+        for (int cb = 0; cb < NDB; ++cb) {
+            bf16x4 wv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[e] = (__bf16)dvt[cb][4 * g + e];
+            *(bf16x4*)(ov + 32 * cb + 8 * g + 4 * lh) = wv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dlam: dlambda_h = -sum over batch and rows of delta_2 (fixed order)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads) void bwd_dlam_kernel(BackwardArgs a) {
+    __shared__ float part[kBwdThreads / 64];
+    const int h = blockIdx.x;
+    const int64_t BH = (int64_t)a.B * a.H;
+    float s = 0.f;
+    for (int b = 0; b < a.B; ++b) {
+        const float* d2 = a.delta + (BH + (int64_t)b * a.H + h) * a.Nq;
+        for (int i = threadIdx.x; i < a.Nq; i += kBwdThreads) s += d2[i];
+    }
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.f;
+        for (int w = 0; w < kBwdThreads / 64; ++w) t += part[w];
+        a.dlam[h] = -t;
+    }
+}
+
+template <int D, int DV>
+hipError_t launch_dims(const BackwardArgs& a, bool causal, hipStream_t stream) {
+    BackwardArgs copy = a;
+    void* args[] = {&copy};
+    const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+    const int64_t BH = (int64_t)a.B * a.H;
+    const int64_t g_prep = (rows + 3) / 4;
+    const int64_t g_dq = (int64_t)((a.Nq + 63) / 64) * BH;
+    const int64_t g_kv = (int64_t)((a.Nk + 127) / 128) * BH;
+    if (g_prep > 0x7fffffff || g_dq > 0x7fffffff || g_kv > 0x7fffffff) return hipErrorInvalidValue;
+    hipError_t e = hipLaunchKernel((const void*)bwd_prep_kernel<DV>, dim3((unsigned)g_prep),
+                                   dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel(causal ? (const void*)bwd_dq_kernel<D, DV, true>
+                               : (const void*)bwd_dq_kernel<D, DV, false>,
+                        dim3((unsigned)g_dq), dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel(causal ? (const void*)bwd_dkdv_kernel<D, DV, true>
+                               : (const void*)bwd_dkdv_kernel<D, DV, false>,
+                        dim3((unsigned)g_kv), dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel((const void*)bwd_dlam_kernel, dim3((unsigned)a.H), dim3(kBwdThreads),
+                           args, 0, stream);
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int dv) {
+    const size_t dd = ((size_t)(B * H * Nq * dv * 2) + 255) / 256 * 256;
+    return dd + (size_t)(2 * B * H * Nq) * sizeof(float);
+}
+
+hipError_t launch_backward_bf16(const BackwardArgs& a, int d, int dv, bool causal,
+                                hipStream_t stream) {
+    if (d == 32 && dv == 64) return launch_dims<32, 64>(a, causal, stream);
+    if (d == 64 && dv == 128) return launch_dims<64, 128>(a, causal, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn

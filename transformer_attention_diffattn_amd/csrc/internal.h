@@ -22,6 +22,38 @@ struct PrefillArgs {
     float eps;
     float scale_log2;  // log2(e) / sqrt(d): folds the score scale into exp2
     uint32_t flags;
+    // training forward only (NULL otherwise): D before the GroupNorm
+    // [B][H][Nq][dv] fp32 and the natural-log log-sum-exp of each score row
+    // [2][B][H][Nq] fp32 (map 1, then map 2)
+    float* d_save;
+    float* lse;
+};
+
+// Arguments of the backward kernels.  Pointers are device memory; layouts as
+// in diffattn.h.
+struct BackwardArgs {
+    const void* q1;
+    const void* q2;
+    const void* k1;
+    const void* k2;
+    const void* v;
+    const float* lam;
+    const void* dout;    // [B][H][Nq][dv]
+    const float* d_save; // [B][H][Nq][dv]
+    const float* lse;    // [2][B][H][Nq]
+    void* dq1;
+    void* dq2;
+    void* dk1;
+    void* dk2;
+    void* dv;
+    float* dlam;         // [H]
+    void* dd;            // workspace: dD [B][H][Nq][dv] bf16
+    float* delta;        // workspace: [2][B][H][Nq] row terms sum_j P_k dP
+    int32_t B, H, Nq, Nk;
+    float lambda_init;
+    float eps;
+    float scale_log2;
+    uint32_t flags;
 };
 
 // Arguments of the decode kernels.
@@ -53,6 +85,11 @@ hipError_t launch_prefill_bf16_wide(const PrefillArgs& a, int d, int dv, bool ca
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);
+hipError_t launch_backward_bf16(const BackwardArgs& a, int d, int dv, bool causal,
+                                hipStream_t stream);
+// Workspace bytes of the backward: dD in bf16, then the row terms (256-byte
+// aligned sections).
+size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int dv);
 
 // Compute units of the current device (cached per device); 0 if unknown.
 int device_cus();

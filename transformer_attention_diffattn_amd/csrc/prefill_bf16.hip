@@ -630,6 +630,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
             }
         }
     }
+    if (a.lse) {
+        // training forward: D before the normalisation, and each map's
+        // log-sum-exp (m and l share the lazy maximum, so m + log2 l is exact)
+        if (qrow < a.Nq) {
+            float* drow = a.d_save + ((size_t)bh * a.Nq + qrow) * DV + map * (DV / 2);
+#pragma unroll
+            for (int db = 0; db < NH; ++db) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(float4*)(drow + 32 * db + 8 * g + 4 * lh) =
+                        make_float4(x[db][4 * g], x[db][4 * g + 1], x[db][4 * g + 2], x[db][4 * g + 3]);
+            }
+            if (lh == 0)
+                a.lse[((size_t)map * a.B * a.H + bh) * a.Nq + qrow] =
+                    (m + __builtin_amdgcn_logf(L)) * 0.69314718055994531f;
+        }
+    }
     if (!(a.flags & 1u)) {
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
