@@ -12,8 +12,11 @@ seeded, and resident in HBM before timing starts.  The throughput counts
 
 The same run also times the decode kernels (split-K partials + merge) on the
 decode workload (B64 H32, one query against an 8192-entry KV cache) and
-reports them in "decode" as GB/s of algorithmic cache traffic, and times the
-fp64 CPU oracle on a bounded sample of the headline workload ("cpu_baseline").
+reports them in "decode" as GB/s of algorithmic cache traffic, times the
+backward (diffattn_bwd after the training forward) on the headline workload
+("backward", TFLOP/s at 12 d + 4 dv flops per unmasked pair: both score maps
+recomputed, one shared dP, dV, dK1, dK2, dQ1, dQ2), and times the fp64 CPU
+oracle on a bounded sample of the headline workload ("cpu_baseline").
 
 Prints one JSON line on stdout.
 """
@@ -102,6 +105,41 @@ def bench_decode(w, steps: int, warmup: int):
     return kern_ms, splits, ws_bytes
 
 
+def bench_backward(w, steps: int, warmup: int):
+    """ms per diffattn_bwd call and per training-forward call on workload w."""
+    import torch
+
+    import transformer_attention_diffattn_amd as da
+    import workloads
+
+    x = workloads.make_prefill(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(1)
+    dout = torch.randn((w.B, w.H, w.nq, w.dv), generator=g, device="cuda").to(w.torch_dtype)
+    args = (x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"])
+    _, d_save, lse = da.fwd_train(*args, lambda_init=w.lambda_init, causal=w.causal, eps=w.eps)
+    ws = torch.empty((max(da.bwd_workspace_size(w.B, w.H, w.nq, w.nk, w.d, w.dv), 16),),
+                     dtype=torch.uint8, device="cuda")
+
+    def bwd_step():
+        da.bwd(*args, dout, d_save, lse, lambda_init=w.lambda_init, causal=w.causal, eps=w.eps,
+               workspace=ws)
+
+    def fwd_step():
+        da.fwd_train(*args, lambda_init=w.lambda_init, causal=w.causal, eps=w.eps)
+
+    for _ in range(warmup):
+        bwd_step()
+    torch.cuda.synchronize()
+    bwd_ms = _events_time(bwd_step, steps)
+    for _ in range(max(2, warmup // 4)):
+        fwd_step()
+    torch.cuda.synchronize()
+    fwd_ms = _events_time(fwd_step, steps)
+    del x, dout, d_save, lse, ws
+    torch.cuda.empty_cache()
+    return bwd_ms, fwd_ms
+
+
 def cpu_baseline(w, budget_s: float = 30.0):
     """Times the fp64 oracle (as it is) head by head over the workload, stopping
     after about budget_s seconds of compute or when every head is done; reports
@@ -184,6 +222,7 @@ def main():
     ap.add_argument("--workload", default="causal_prefill_bf16")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain fp32 copy of 1 GiB (3 times), the reference the "
                          "HBM byte counters are scaled by")
@@ -267,6 +306,24 @@ def main():
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": _traffic("decode_partial_kernel"),
                          "bytes_per_call": nbytes},
+        }
+
+    if not args.no_backward and w.dtype == "bf16" and (w.d, w.dv) in ((32, 64), (64, 128)):
+        bms, tfms = bench_backward(w, max(5, args.steps // 5), max(3, args.warmup // 20))
+        pairs = flops / (4 * (w.d + w.dv))
+        bflops = pairs * (12 * w.d + 4 * w.dv)
+        btf = bflops / (bms * 1e-3) / 1e12
+        rec["backward"] = {
+            "workload": w.name,
+            "value": round(btf, 2),
+            "unit": "TFLOP/s",
+            "ms_per_call": round(bms, 4),
+            "flops_per_call": int(bflops),
+            "fwd_train_ms": round(tfms, 4),
+            "roofline": {"bound": "mfma", "kernel": "bwd_prep + bwd_dq + bwd_dkdv + bwd_dlam",
+                         "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
         }
 
     if not args.no_cpu:

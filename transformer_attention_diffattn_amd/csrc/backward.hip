@@ -86,20 +86,34 @@ __device__ __forceinline__ void pack(const float (&x)[16], bf16x8 (&o)[2]) {
         for (int j = 0; j < 8; ++j) o[c][j] = (__bf16)x[8 * c + j];
 }
 
-// rows [row0, row0 + rows) of a [n][W] bf16 tensor into a padded LDS tile;
-// rows at or past n are zero
+// A tile of 32 rows of a [n][W] bf16 tensor, moved in two steps so that the
+// global loads of the next tile are in flight while the current one is used:
+// load() into registers (rows at or past n read as zero), store() into a
+// padded LDS tile.
 template <int W>
-__device__ __forceinline__ void stage_rows(uint16_t* t, const uint16_t* g, int64_t row0, int rows,
-                                           int64_t n) {
-    constexpr int kStride = W + 8;
-    constexpr int kCpr = W / 8;  // 16-byte chunks per row
-    for (int c = threadIdx.x; c < rows * kCpr; c += kBwdThreads) {
-        const int r = c / kCpr, ch = c % kCpr;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row0 + r < n) v = *(const uint4*)(g + (row0 + r) * W + 8 * ch);
-        *(uint4*)(t + r * kStride + 8 * ch) = v;
+struct RowTile {
+    static constexpr int kCpr = W / 8;  // 16-byte chunks per row
+    static constexpr int kChunks = 32 * kCpr;
+    static constexpr int kPer = (kChunks + kBwdThreads - 1) / kBwdThreads;
+    uint4 r[kPer];
+    __device__ __forceinline__ void load(const uint16_t* g, int64_t row0, int64_t n) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + kBwdThreads * i;
+            const int row = c / kCpr, ch = c % kCpr;
+            r[i] = (c < kChunks && row0 + row < n)
+                       ? *(const uint4*)(g + (row0 + row) * W + 8 * ch)
+                       : make_uint4(0, 0, 0, 0);
+        }
     }
-}
+    __device__ __forceinline__ void store(uint16_t* t) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + kBwdThreads * i;
+            if (c < kChunks) *(uint4*)(t + (c / kCpr) * (W + 8) + 8 * (c % kCpr)) = r[i];
+        }
+    }
+};
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -164,8 +178,9 @@ template <int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
     constexpr int NKB = D / 16, NVB = DV / 16, NCB = D / 32;
     constexpr int KS = D + 8, VS = DV + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][32 * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[32 * VS];
+    // two buffers, each K1 | K2 | V of one 32-key tile
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][2][32 * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[2][32 * VS];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, lh = lane >> 5;
@@ -204,25 +219,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
 
     const int nkt_all = (a.Nk + 31) / 32;
     const int nkt = CAUSAL ? min(nkt_all, (qt * 64 + 64 + 31) / 32) : nkt_all;
+    RowTile<D> t1, t2;
+    RowTile<DV> tv;
+    t1.load(gk1, 0, a.Nk);
+    t2.load(gk2, 0, a.Nk);
+    tv.load(gv, 0, a.Nk);
+    t1.store(sk[0][0]);
+    t2.store(sk[0][1]);
+    tv.store(sv[0]);
+    __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
-        stage_rows<D>(sk[0], gk1, (int64_t)kt * 32, 32, a.Nk);
-        stage_rows<D>(sk[1], gk2, (int64_t)kt * 32, 32, a.Nk);
-        stage_rows<DV>(sv, gv, (int64_t)kt * 32, 32, a.Nk);
-        __syncthreads();
-        const uint16_t* kt_ = sk[map];
+        const int buf = kt & 1;
+        const bool more = kt + 1 < nkt;
+        if (more) {  // next tile's loads fly while this one is used
+            t1.load(gk1, (int64_t)(kt + 1) * 32, a.Nk);
+            t2.load(gk2, (int64_t)(kt + 1) * 32, a.Nk);
+            tv.load(gv, (int64_t)(kt + 1) * 32, a.Nk);
+        }
+        const uint16_t* kt_ = sk[buf][map];
+        const uint16_t* sv_ = sv[buf];
         // S^T = K Q^T and dP^T = V dD^T, key rows in swap23 order
         f32x16 s = f32x16{}, dp = f32x16{};
         const int kr = swap23(l32);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s = mfma(rd_row(kt_, KS, kr, 16 * kb, lh), qf[kb], s);
 #pragma unroll
-        for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sv, VS, kr, 16 * c, lh), df[c], dp);
+        for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sv_, VS, kr, 16 * c, lh), df[c], dp);
         float p[16], w[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kt * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
             const bool ok = qok && key < a.Nk && (!CAUSAL || key <= qrow);
-            p[r] = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse2)) : 0.f;
+            float x = fmaf(s[r], sl2, -lse2);
+            asm volatile("" : "+v"(x));  // formed for every lane (no branch)
+            p[r] = __builtin_amdgcn_exp2f(ok ? x : -INFINITY);
             w[r] = p[r] * dp[r];
             dsum += w[r];
         }
@@ -238,6 +268,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
                 xt[cb] = mfma(kc, pw[kk], xt[cb]);
                 yt[cb] = mfma(kc, pp[kk], yt[cb]);
             }
+        }
+        // the other buffer was last read before the previous barrier
+        if (more) {
+            t1.store(sk[buf ^ 1][0]);
+            t2.store(sk[buf ^ 1][1]);
+            tv.store(sv[buf ^ 1]);
         }
         __syncthreads();
     }
@@ -270,9 +306,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 void bwd_dkdv_kernel(BackwardArgs a) {
     constexpr int NKB = D / 16, NVB = DV / 16, NCB = D / 32, NDB = DV / 32;
     constexpr int KS = D + 8, VS = DV + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sq[2][32 * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t sd[32 * VS];
-    __shared__ __attribute__((aligned(16))) float srow[4][32];  // lse1, lse2 (log2), delta1, delta2
+    // two buffers, each Q1 | Q2 | dD and the row terms of one 32-query tile
+    __shared__ __attribute__((aligned(16))) uint16_t sq[2][2][32 * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t sd[2][32 * VS];
+    // per query: lse1, lse2 (log2 units), delta1, delta2 -- one 16-byte read
+    __shared__ __attribute__((aligned(16))) float4 srow[2][32];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, lh = lane >> 5;
@@ -317,39 +355,71 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     const float* lse2 = a.lse + ((size_t)BH + bh) * a.Nq;
     const float* del1 = a.delta + (size_t)bh * a.Nq;
     const float* del2 = a.delta + ((size_t)BH + bh) * a.Nq;
+    // row terms: thread t < 128 carries term t / 32 of query t % 32
+    const int which = threadIdx.x >> 5;
+    auto put_row = [&](int b, float v) {
+        if (threadIdx.x < 128) ((float*)&srow[b][threadIdx.x & 31])[which] = v;
+    };
+    const float* rsrc = which == 0 ? lse1 : which == 1 ? lse2 : which == 2 ? del1 : del2;
+    auto load_row = [&](int qt) {
+        const int q = qt * 32 + (threadIdx.x & 31);
+        const float v = (threadIdx.x < 128 && q < a.Nq) ? rsrc[q] : 0.f;
+        return which < 2 ? v * kLog2e : v;
+    };
+    RowTile<D> t1, t2;
+    RowTile<DV> td;
+    float rv = 0.f;
+    if (qt0 < nqt) {
+        t1.load(gq1, (int64_t)qt0 * 32, a.Nq);
+        t2.load(gq2, (int64_t)qt0 * 32, a.Nq);
+        td.load(gdd, (int64_t)qt0 * 32, a.Nq);
+        rv = load_row(qt0);
+        t1.store(sq[0][0]);
+        t2.store(sq[0][1]);
+        td.store(sd[0]);
+        put_row(0, rv);
+    }
+    __syncthreads();
     for (int qt = qt0; qt < nqt; ++qt) {
-        stage_rows<D>(sq[0], gq1, (int64_t)qt * 32, 32, a.Nq);
-        stage_rows<D>(sq[1], gq2, (int64_t)qt * 32, 32, a.Nq);
-        stage_rows<DV>(sd, gdd, (int64_t)qt * 32, 32, a.Nq);
-        if (threadIdx.x < 128) {
-            const int which = threadIdx.x >> 5, i = threadIdx.x & 31;
-            const int q = qt * 32 + i;
-            const float* src = which == 0 ? lse1 : which == 1 ? lse2 : which == 2 ? del1 : del2;
-            const float v = q < a.Nq ? src[q] : 0.f;
-            srow[which][i] = which < 2 ? v * kLog2e : v;
+        const int buf = (qt - qt0) & 1;
+        const bool more = qt + 1 < nqt;
+        if (more) {  // next tile's loads fly while this one is used
+            t1.load(gq1, (int64_t)(qt + 1) * 32, a.Nq);
+            t2.load(gq2, (int64_t)(qt + 1) * 32, a.Nq);
+            td.load(gdd, (int64_t)(qt + 1) * 32, a.Nq);
+            rv = load_row(qt + 1);
         }
-        __syncthreads();
+        const uint16_t* sq1 = sq[buf][0];
+        const uint16_t* sq2 = sq[buf][1];
+        const uint16_t* sd_ = sd[buf];
+        const float4* sr = srow[buf];
         // S_k = Q_k K_k^T and dP = dD V^T, query rows in swap23 order
         const int qr = swap23(l32);
         f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            s1 = mfma(rd_row(sq[0], KS, qr, 16 * kb, lh), k1f[kb], s1);
-            s2 = mfma(rd_row(sq[1], KS, qr, 16 * kb, lh), k2f[kb], s2);
+            s1 = mfma(rd_row(sq1, KS, qr, 16 * kb, lh), k1f[kb], s1);
+            s2 = mfma(rd_row(sq2, KS, qr, 16 * kb, lh), k2f[kb], s2);
         }
 #pragma unroll
-        for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sd, VS, qr, 16 * c, lh), vf[c], dp);
+        for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sd_, VS, qr, 16 * c, lh), vf[c], dp);
         float wd[16], d1[16], d2[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
             const int q = qt * 32 + qi;
             const bool ok = kok && q < a.Nq && (!CAUSAL || key <= q);
-            const float p1 = ok ? __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, -srow[0][qi])) : 0.f;
-            const float p2 = ok ? __builtin_amdgcn_exp2f(fmaf(s2[r], sl2, -srow[1][qi])) : 0.f;
+            const float4 t = sr[qi];
+            // masked pairs take exp2(-inf) = 0; the arguments are formed for
+            // every lane (the empty asm keeps the compiler from moving them,
+            // and the row-term read, into a branch per element)
+            float x1 = fmaf(s1[r], sl2, -t.x), x2 = fmaf(s2[r], sl2, -t.y);
+            asm volatile("" : "+v"(x1), "+v"(x2));
+            const float p1 = __builtin_amdgcn_exp2f(ok ? x1 : -INFINITY);
+            const float p2 = __builtin_amdgcn_exp2f(ok ? x2 : -INFINITY);
             wd[r] = p1 - lam * p2;
-            d1[r] = p1 * (dp[r] - srow[2][qi]);
-            d2[r] = -lam * p2 * (dp[r] - srow[3][qi]);
+            d1[r] = p1 * (dp[r] - t.z);
+            d2[r] = -lam * p2 * (dp[r] - t.w);
         }
         bf16x8 pwd[2], pd1[2], pd2[2];
         pack(wd, pwd);
@@ -360,12 +430,19 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int cb = 0; cb < NDB; ++cb)
-                dvt[cb] = mfma(rd_col(sd, VS, 16 * kk, 32 * cb, lane), pwd[kk], dvt[cb]);
+                dvt[cb] = mfma(rd_col(sd_, VS, 16 * kk, 32 * cb, lane), pwd[kk], dvt[cb]);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                dk1t[cb] = mfma(rd_col(sq[0], KS, 16 * kk, 32 * cb, lane), pd1[kk], dk1t[cb]);
-                dk2t[cb] = mfma(rd_col(sq[1], KS, 16 * kk, 32 * cb, lane), pd2[kk], dk2t[cb]);
+                dk1t[cb] = mfma(rd_col(sq1, KS, 16 * kk, 32 * cb, lane), pd1[kk], dk1t[cb]);
+                dk2t[cb] = mfma(rd_col(sq2, KS, 16 * kk, 32 * cb, lane), pd2[kk], dk2t[cb]);
             }
+        }
+        // the other buffer was last read before the previous barrier
+        if (more) {
+            t1.store(sq[buf ^ 1][0]);
+            t2.store(sq[buf ^ 1][1]);
+            td.store(sd[buf ^ 1]);
+            put_row(buf ^ 1, rv);
         }
         __syncthreads();
     }
