@@ -28,6 +28,14 @@ scale tau = 1/sqrt(d), c = 1 - lambda_init):
 Dense N x N maps are materialised, so this is for the small shapes the tests
 use.  ``head_lse`` gives the natural-log log-sum-exp of each score row, the
 per-row softmax statistic a training forward keeps for the backward.
+
+Two diagnostics of the maps follow the quantities the pages report for trained
+models -- the share of attention that lands on planted "needles"
+(llmbytes.dev, "Benchmark Performance", multi-needle retrieval) and the top
+attention logit (same page, "Solving the Quantization Crisis"):
+``head_needles`` (each needle's weight in A1 and A2, and its query row's total
+weight on all the head's needle keys) and ``head_row_max`` (each row's largest
+scaled score).
 """
 from __future__ import annotations
 
@@ -138,3 +146,22 @@ def lse(q, k, *, causal: bool) -> np.ndarray:
         for h in range(H):
             out[b, h] = head_lse(q[b, h], k[b, h], causal=causal)
     return out
+
+
+def head_row_max(q, k, *, causal: bool) -> np.ndarray:
+    """Largest scaled score S_ij = q_i . k_j / sqrt(d) over the keys row i sees
+    (the row's top attention logit), fp64 [Nq]."""
+    return _scores(_f64(q), _f64(k), causal).max(axis=1)
+
+
+def head_needles(q1, q2, k1, k2, needle_q, needle_k, *, causal: bool) -> np.ndarray:
+    """For needle r (query needle_q[r], key needle_k[r]) of one head: A1 and A2
+    at (query, key), and the query row's total A1 and A2 weight on all of the
+    head's needle keys it sees.  fp64 [n, 4]."""
+    q1, q2, k1, k2 = (_f64(t) for t in (q1, q2, k1, k2))
+    nq = np.asarray(needle_q, dtype=np.int64)
+    nk = np.asarray(needle_k, dtype=np.int64)
+    a1 = _softmax_rows(_scores(q1, k1, causal))[nq]
+    a2 = _softmax_rows(_scores(q2, k2, causal))[nq]
+    r = np.arange(len(nq))
+    return np.stack([a1[r, nk], a2[r, nk], a1[:, nk].sum(axis=1), a2[:, nk].sum(axis=1)], axis=1)

@@ -165,3 +165,28 @@ def test_planted_backward_mistake_is_caught(old, new):
     exec(compile(src.replace(old, new), "mutant_backward", "exec"), mod.__dict__)
     with pytest.raises(AssertionError):
         check_against_autograd(mod)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_diagnostics_match_library_softmax_and_max(causal):
+    n, d = 40, 16
+    q1, q2, k1, k2 = (_rand((n, d), 90 + i) for i in range(4))
+    nk = np.array([3, 17, 25, 39])
+    nq = np.array([5, 30, 25, 39])  # each at or after its key
+    got = obw.head_needles(q1, q2, k1, k2, nq, nk, causal=causal)
+    mask = torch.tril(torch.ones(n, n, dtype=torch.bool)) if causal else None
+    for col, (q, k) in enumerate(((q1, k1), (q2, k2))):
+        s = torch.tensor(q) @ torch.tensor(k).T / np.sqrt(d)
+        if causal:
+            s = s.masked_fill(~mask, float("-inf"))
+        a = torch.softmax(s, dim=-1).numpy()
+        np.testing.assert_allclose(got[:, col], a[nq, nk], rtol=1e-12)
+        np.testing.assert_allclose(got[:, 2 + col], a[nq][:, nk].sum(axis=1), rtol=1e-12)
+        np.testing.assert_allclose(obw.head_row_max(q, k, causal=causal),
+                                   torch.amax(s, dim=-1).numpy(), rtol=1e-13)
+    # the top logit never exceeds the row's log-sum-exp, nor falls more than
+    # log(visible keys) below it
+    lse = obw.head_lse(q1, k1, causal=causal)
+    mx = obw.head_row_max(q1, k1, causal=causal)
+    vis = np.arange(1, n + 1) if causal else np.full(n, n)
+    assert np.all(mx <= lse + 1e-12) and np.all(mx >= lse - np.log(vis) - 1e-12)
