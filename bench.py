@@ -15,8 +15,11 @@ decode workload (B64 H32, one query against an 8192-entry KV cache) and
 reports them in "decode" as GB/s of algorithmic cache traffic, times the
 backward (diffattn_bwd after the training forward) on the headline workload
 ("backward", TFLOP/s at 12 d + 4 dv flops per unmasked pair: both score maps
-recomputed, one shared dP, dV, dK1, dK2, dQ1, dQ2), and times the fp64 CPU
-oracle on a bounded sample of the headline workload ("cpu_baseline").
+recomputed, one shared dP, dV, dK1, dK2, dQ1, dQ2), runs the map
+diagnostics on the 32K needle workload ("diagnostics": the row-max sweep at
+4 d flops per unmasked pair, the needle weights, and the values they give on
+those synthetic inputs), and times the fp64 CPU oracle on a bounded sample of
+the headline workload ("cpu_baseline").
 
 Prints one JSON line on stdout.
 """
@@ -140,6 +143,52 @@ def bench_backward(w, steps: int, warmup: int):
     return bwd_ms, fwd_ms
 
 
+def bench_diag(steps: int):
+    """Map diagnostics on the 32K needle workload: kernel times and values."""
+    import numpy as np
+    import torch
+
+    import transformer_attention_diffattn_amd as da
+    import workloads
+
+    w = workloads.get("long_needles_bf16")
+    x = workloads.make_prefill(w, device="cuda")
+    args = (x["q1"], x["q2"], x["k1"], x["k2"], x["v"])
+    _, _, lse = da.fwd_train(*args, x["lam"], lambda_init=w.lambda_init, causal=True, eps=w.eps)
+    plans = workloads.needle_plan(w)
+    nq = torch.tensor(np.stack([p[1] for p in plans]).reshape(w.B, w.H, -1), dtype=torch.int32)
+    nk = torch.tensor(np.stack([p[0] for p in plans]).reshape(w.B, w.H, -1), dtype=torch.int32)
+    nq, nk = nq.cuda(), nk.cuda()
+    da.diag(*args, causal=True)  # warm-up
+    rm_ms = _events_time(lambda: da.diag(*args, causal=True), steps)
+    nd_ms = _events_time(lambda: da.diag(*args, causal=True, lse=lse, needle_q=nq, needle_k=nk,
+                                          row_max=False), steps)
+    rm, nd = da.diag(*args, causal=True, lse=lse, needle_q=nq, needle_k=nk)
+    torch.cuda.synchronize()
+    lam = x["lam"].view(1, w.H, 1)
+    a1, a2 = nd[..., 0], nd[..., 1]
+    m1, m2 = nd[..., 2], nd[..., 3]
+    flops = w.pairs() * 4 * w.d
+    out = {
+        "workload": w.name,
+        "row_max_ms": round(rm_ms, 4),
+        "row_max_tflops": round(flops / (rm_ms * 1e-3) / 1e12, 2),
+        "needles_ms": round(nd_ms, 4),
+        "values": {
+            "needle_weight_map1_mean": round(float(a1.mean()), 5),
+            "needle_weight_map2_mean": round(float(a2.mean()), 6),
+            "needle_weight_differential_mean": round(float((a1 - lam * a2).mean()), 5),
+            "needle_row_mass_map1_mean": round(float(m1.mean()), 5),
+            "needle_row_mass_differential_mean": round(float((m1 - lam * m2).mean()), 5),
+            "top_logit_map1": round(float(rm[0].max()), 3),
+            "top_logit_map2": round(float(rm[1].max()), 3),
+        },
+    }
+    del x, lse, rm, nd
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, budget_s: float = 30.0):
     """Times the fp64 oracle (as it is) head by head over the workload, stopping
     after about budget_s seconds of compute or when every head is done; reports
@@ -223,6 +272,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-diag", action="store_true", help="skip the diagnostics leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain fp32 copy of 1 GiB (3 times), the reference the "
                          "HBM byte counters are scaled by")
@@ -325,6 +375,9 @@ def main():
                          "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
                          "traffic": None},
         }
+
+    if not args.no_diag:
+        rec["diagnostics"] = bench_diag(max(3, args.steps // 20))
 
     if not args.no_cpu:
         cb = cpu_baseline(w)

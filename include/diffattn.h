@@ -142,6 +142,26 @@ int diffattn_bwd(const void* q1, const void* q2, const void* k1, const void* k2,
                  const diffattn_dims* dims, void* stream);
 
 /*
+ * Diagnostics of the two softmax maps (bf16; any supported head_dim), the
+ * quantities the pages report for trained models (llmbytes.dev, "Benchmark
+ * Performance": attention share on needles; "Solving the Quantization
+ * Crisis": top attention logit):
+ *   row_max [2][B][H][seq_q] fp32 (or NULL): each query row's largest scaled
+ *     score q.k/sqrt(d) over the keys it sees, map 1 then map 2;
+ *   needles [B][H][n_needles][4] fp32 (or NULL): for planted pair r of a head
+ *     (query needle_q[b][h][r], key needle_k[b][h][r], int32 device arrays),
+ *     the weight of the pair in A1 and in A2, and the query row's total A1
+ *     and A2 weight on all of the head's needle keys it sees; needs lse from
+ *     diffattn_fwd_train with the same inputs.  A pair with an index out of
+ *     range gets NaNs.  1 <= n_needles <= 4096.
+ * At least one of row_max and needles must be given.  Allocates nothing.
+ */
+int diffattn_diag(const void* q1, const void* q2, const void* k1, const void* k2,
+                  const float* lse, int causal, const int32_t* needle_q,
+                  const int32_t* needle_k, int32_t n_needles, float* row_max, float* needles,
+                  const diffattn_dims* dims, void* stream);
+
+/*
  * Decode: one new query token per (b, h) against a KV cache.  Every cached
  * position of the sequence is visible (the cache already holds the current
  * token), so no mask applies.

@@ -148,20 +148,33 @@ def lse(q, k, *, causal: bool) -> np.ndarray:
     return out
 
 
-def head_row_max(q, k, *, causal: bool) -> np.ndarray:
+def _score_rows(q, k, rows, causal: bool) -> np.ndarray:
+    """Scaled scores of the listed query rows against every key (-inf where
+    the causal mask hides the key), [len(rows), Nk]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    s = (q[rows] @ k.T) / np.sqrt(q.shape[1])
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] <= rows[:, None], s, -np.inf)
+    return s
+
+
+def head_row_max(q, k, *, causal: bool, rows=None) -> np.ndarray:
     """Largest scaled score S_ij = q_i . k_j / sqrt(d) over the keys row i sees
-    (the row's top attention logit), fp64 [Nq]."""
-    return _scores(_f64(q), _f64(k), causal).max(axis=1)
+    (the row's top attention logit), fp64, for every row or the listed ones."""
+    q, k = _f64(q), _f64(k)
+    rows = np.arange(q.shape[0]) if rows is None else rows
+    return _score_rows(q, k, rows, causal).max(axis=1)
 
 
 def head_needles(q1, q2, k1, k2, needle_q, needle_k, *, causal: bool) -> np.ndarray:
     """For needle r (query needle_q[r], key needle_k[r]) of one head: A1 and A2
     at (query, key), and the query row's total A1 and A2 weight on all of the
-    head's needle keys it sees.  fp64 [n, 4]."""
+    head's needle keys it sees.  Only the needles' query rows are formed.
+    fp64 [n, 4]."""
     q1, q2, k1, k2 = (_f64(t) for t in (q1, q2, k1, k2))
     nq = np.asarray(needle_q, dtype=np.int64)
     nk = np.asarray(needle_k, dtype=np.int64)
-    a1 = _softmax_rows(_scores(q1, k1, causal))[nq]
-    a2 = _softmax_rows(_scores(q2, k2, causal))[nq]
+    a1 = _softmax_rows(_score_rows(q1, k1, nq, causal))
+    a2 = _softmax_rows(_score_rows(q2, k2, nq, causal))
     r = np.arange(len(nq))
     return np.stack([a1[r, nk], a2[r, nk], a1[:, nk].sum(axis=1), a2[:, nk].sum(axis=1)], axis=1)

@@ -184,6 +184,10 @@ def test_diagnostics_match_library_softmax_and_max(causal):
         np.testing.assert_allclose(got[:, 2 + col], a[nq][:, nk].sum(axis=1), rtol=1e-12)
         np.testing.assert_allclose(obw.head_row_max(q, k, causal=causal),
                                    torch.amax(s, dim=-1).numpy(), rtol=1e-13)
+    # row subsets agree with the whole rows
+    sub = np.array([0, 7, 39])
+    np.testing.assert_allclose(obw.head_row_max(q1, k1, causal=causal, rows=sub),
+                               obw.head_row_max(q1, k1, causal=causal)[sub], rtol=0)
     # the top logit never exceeds the row's log-sum-exp, nor falls more than
     # log(visible keys) below it
     lse = obw.head_lse(q1, k1, causal=causal)

@@ -91,6 +91,8 @@ def lib():
         L.diffattn_bwd.restype = I
         L.diffattn_bwd.argtypes = [P, P, P, P, P, P, F, I, P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_size_t, DP, P]
+        L.diffattn_diag.restype = I
+        L.diffattn_diag.argtypes = [P, P, P, P, P, I, P, P, ctypes.c_int32, P, P, DP, P]
         _lib = L
     return _lib
 
@@ -252,6 +254,41 @@ def bwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
                             _stream_ptr(dev))
     _check(st)
     return (*grads, dlam)
+
+
+def diag(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
+         v: torch.Tensor, causal: bool = True, lse: Optional[torch.Tensor] = None,
+         needle_q: Optional[torch.Tensor] = None, needle_k: Optional[torch.Tensor] = None,
+         row_max: bool = True):
+    """Diagnostics of the two maps (bf16).  Returns (row_max [2,B,H,Nq] fp32 or
+    None, needles [B,H,n,4] fp32 or None).  needle_q/needle_k: int [B,H,n]
+    (query, key) pairs; needles need ``lse`` from ``fwd_train``.  v only
+    supplies dv for the size checks."""
+    B, H, Nq, Nk, d, dv = _check_inputs(q1, q2, k1, k2, v)
+    dev = q1.device
+    rm = torch.empty((2, B, H, Nq), dtype=torch.float32, device=dev) if row_max else None
+    nd = None
+    n = 0
+    if needle_q is not None:
+        _require(lse is not None and lse.shape == (2, B, H, Nq) and lse.dtype == torch.float32,
+                 "needles need the fp32 [2,B,H,Nq] lse of fwd_train")
+        needle_q = needle_q.to(device=dev, dtype=torch.int32).contiguous()
+        needle_k = needle_k.to(device=dev, dtype=torch.int32).contiguous()
+        _require(needle_q.dim() == 3 and needle_q.shape[:2] == (B, H)
+                 and needle_k.shape == needle_q.shape, "needle_q/needle_k must be [B,H,n]")
+        n = needle_q.shape[2]
+        nd = torch.empty((B, H, n, 4), dtype=torch.float32, device=dev)
+    dims = Dims(B, H, Nq, Nk, d, dv, _dtype_code(q1), 1e-5, 0)
+    st = lib().diffattn_diag(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
+                             lse.data_ptr() if (lse is not None and nd is not None) else None,
+                             int(bool(causal)),
+                             needle_q.data_ptr() if nd is not None else None,
+                             needle_k.data_ptr() if nd is not None else None, n,
+                             rm.data_ptr() if rm is not None else None,
+                             nd.data_ptr() if nd is not None else None,
+                             ctypes.byref(dims), _stream_ptr(dev))
+    _check(st)
+    return rm, nd
 
 
 def _decode_dims(B, H, L, d, dv, dtype_code, eps, pre_norm) -> Dims:

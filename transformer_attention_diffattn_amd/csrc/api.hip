@@ -251,6 +251,44 @@ int diffattn_bwd(const void* q1, const void* q2, const void* k1, const void* k2,
     return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
 }
 
+int diffattn_diag(const void* q1, const void* q2, const void* k1, const void* k2,
+                  const float* lse, int causal, const int32_t* needle_q,
+                  const int32_t* needle_k, int32_t n_needles, float* row_max, float* needles,
+                  const diffattn_dims* dims, void* stream) {
+    int st = check_dims(dims);
+    if (st != DIFFATTN_OK) return st;
+    if (dims->dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
+    if (causal && dims->seq_q != dims->seq_k) return DIFFATTN_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q1, q2, k1, k2};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return DIFFATTN_ERR_INVALID;
+    if (n_needles < 0 || n_needles > 4096) return DIFFATTN_ERR_INVALID;
+    if (!row_max && !needles) return DIFFATTN_ERR_INVALID;
+    if (row_max && ((uintptr_t)row_max & 3u)) return DIFFATTN_ERR_INVALID;
+    if (needles) {
+        if (n_needles < 1 || !lse || !needle_q || !needle_k) return DIFFATTN_ERR_INVALID;
+        if (((uintptr_t)lse | (uintptr_t)needle_q | (uintptr_t)needle_k | (uintptr_t)needles) & 3u)
+            return DIFFATTN_ERR_INVALID;
+    }
+    DiagArgs a;
+    a.q1 = q1;
+    a.q2 = q2;
+    a.k1 = k1;
+    a.k2 = k2;
+    a.lse = lse;
+    a.needle_q = needle_q;
+    a.needle_k = needle_k;
+    a.row_max = row_max;
+    a.needles = needles;
+    a.n_needles = needles ? n_needles : 0;
+    a.B = dims->batch;
+    a.H = dims->heads;
+    a.Nq = dims->seq_q;
+    a.Nk = dims->seq_k;
+    const hipError_t e = launch_diag_bf16(a, dims->head_dim, causal != 0, (hipStream_t)stream);
+    return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
+}
+
 int32_t diffattn_decode_default_splits(const diffattn_dims* dims) {
     if (check_decode_dims(dims) != DIFFATTN_OK) return 0;
     return resolve_splits(dims, 0);

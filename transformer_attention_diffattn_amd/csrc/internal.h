@@ -56,6 +56,21 @@ struct BackwardArgs {
     uint32_t flags;
 };
 
+// Arguments of the diagnostics kernels.
+struct DiagArgs {
+    const void* q1;
+    const void* q2;
+    const void* k1;
+    const void* k2;
+    const float* lse;         // [2][B][H][Nq] from the training forward (needles only)
+    const int32_t* needle_q;  // [B][H][n]
+    const int32_t* needle_k;  // [B][H][n]
+    float* row_max;           // [2][B][H][Nq] or NULL
+    float* needles;           // [B][H][n][4] or NULL
+    int32_t n_needles;
+    int32_t B, H, Nq, Nk;
+};
+
 // Arguments of the decode kernels.
 struct DecodeArgs {
     const void* q1;
@@ -87,6 +102,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);
 hipError_t launch_backward_bf16(const BackwardArgs& a, int d, int dv, bool causal,
                                 hipStream_t stream);
+hipError_t launch_diag_bf16(const DiagArgs& a, int d, bool causal, hipStream_t stream);
 // Workspace bytes of the backward: dD in bf16, then the row terms (256-byte
 // aligned sections).
 size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int dv);
