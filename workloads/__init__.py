@@ -34,7 +34,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_prefill", "make_decode", "make", "needle_plan"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_prefill", "make_decode", "make", "needle_plan",
+           "quantize_e4m3", "make_prefill_fp8"]
 
 
 @dataclass(frozen=True)
@@ -315,3 +316,34 @@ def _device_draw(w: Workload, dev: torch.device, names, shapes):
         out[n] = x.to(dt)
         del x
     return out
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) query/key inputs
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor E4M3 codes of x: scale = max|x| / 448 (1 if x is all zero),
+    codes = x / scale rounded by torch's float8_e4m3fn conversion (nearest,
+    ties to even).  Returns (codes as float8_e4m3fn, scale as a Python float).
+    Input preparation only: whoever consumes the codes decodes them itself."""
+    amax = float(x.abs().max().float()) if x.numel() else 0.0
+    scale = amax / E4M3_MAX if amax > 0 else 1.0
+    codes = (x.float() / scale).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return codes, scale
+
+
+def make_prefill_fp8(w: Workload, device: str | torch.device = "cpu", seed: Optional[int] = None):
+    """Inputs of a prefill workload with FP8 queries and keys: the tensors of
+    make_prefill (bf16 V), with q1, q2, k1, k2 replaced by their E4M3 codes and
+    ``scales`` = [s_q1, s_q2, s_k1, s_k2]."""
+    x = make_prefill(w, device, seed)
+    scales = []
+    for n in ("q1", "q2", "k1", "k2"):
+        x[n], s = quantize_e4m3(x[n])
+        scales.append(s)
+    x["scales"] = scales
+    return x
