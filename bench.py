@@ -18,7 +18,8 @@ backward (diffattn_bwd after the training forward) on the headline workload
 recomputed, one shared dP, dV, dK1, dK2, dQ1, dQ2), runs the map
 diagnostics on the 32K needle workload ("diagnostics": the row-max sweep at
 4 d flops per unmasked pair, the needle weights, and the values they give on
-those synthetic inputs), and times the fp64 CPU oracle on a bounded sample of
+those synthetic inputs), times the prefill with Q and K quantised to E4M3
+("fp8_qk"), and times the fp64 CPU oracle on a bounded sample of
 the headline workload ("cpu_baseline").
 
 Prints one JSON line on stdout.
@@ -262,6 +263,40 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def bench_fp8(w, steps: int, warmup: int):
+    """ms per diffattn_fwd_fp8 launch on workload w with Q1, Q2, K1, K2
+    quantised per tensor to E4M3 (V stays bf16), and ms per bf16 launch on
+    the unquantised inputs timed alternately with it (same clocks)."""
+    import torch
+
+    import transformer_attention_diffattn_amd as da
+    import workloads
+
+    x = workloads.make_prefill(w, device="cuda")
+    x8 = workloads.make_prefill_fp8(w, device="cuda")
+    out = torch.empty((w.B, w.H, w.nq, w.dv), dtype=torch.bfloat16, device="cuda")
+
+    def step8():
+        da.fwd_fp8(x8["q1"], x8["q2"], x8["k1"], x8["k2"], x8["v"], x8["scales"], x8["lam"],
+                   lambda_init=w.lambda_init, causal=w.causal, eps=w.eps, out=out)
+
+    def step16():
+        da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], lambda_init=w.lambda_init,
+               causal=w.causal, eps=w.eps, out=out)
+
+    for _ in range(warmup):
+        step8()
+        step16()
+    torch.cuda.synchronize()
+    t8, t16 = [], []
+    for _ in range(3):
+        t8.append(_events_time(step8, steps))
+        t16.append(_events_time(step16, steps))
+    del x, x8, out
+    torch.cuda.empty_cache()
+    return min(t8), min(t16)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +308,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-diag", action="store_true", help="skip the diagnostics leg")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 query/key leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain fp32 copy of 1 GiB (3 times), the reference the "
                          "HBM byte counters are scaled by")
@@ -373,6 +409,26 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "bwd_prep + bwd_dq + bwd_dkdv + bwd_dlam",
                          "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+        }
+
+    if not args.no_fp8 and w.dtype == "bf16" and (w.d, w.dv) == (64, 128):
+        fms, bms16 = bench_fp8(w, max(10, args.steps // 3), max(20, args.warmup // 5))
+        pairs = flops / (4 * (w.d + w.dv))
+        # scores on the e4m3 MFMA (peak 2x bf16), P.V on the bf16 one: the
+        # peak of this mix is the flops over their time at the two peaks
+        mix_peak = flops / (pairs * (4 * w.d / (2 * PEAK_BF16_TFLOPS) + 4 * w.dv / PEAK_BF16_TFLOPS))
+        ftf = flops / (fms * 1e-3) / 1e12
+        rec["fp8_qk"] = {
+            "workload": w.name + " (Q, K as e4m3, per-tensor scales)",
+            "value": round(ftf, 2),
+            "unit": "TFLOP/s",
+            "ms_per_call": round(fms, 4),
+            "bf16_ms_per_call_same_run": round(bms16, 4),
+            "speedup_vs_bf16": round(bms16 / fms, 3),
+            "roofline": {"bound": "mfma", "kernel": "prefill_fp8qk_kernel",
+                         "achieved": round(ftf, 2), "peak": round(mix_peak, 1),
+                         "unit": "TFLOP/s", "frac": round(ftf / mix_peak, 4),
                          "traffic": None},
         }
 

@@ -97,6 +97,30 @@ int diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
                  void* out, const diffattn_dims* dims, void* stream);
 
 /*
+ * Prefill with FP8 query and key operands.  Among the low-bit formats that
+ * the smaller attention-logit outliers of differential attention make usable,
+ * the pages name FP8 (llmbytes.dev, "Solving the Quantization Crisis").
+ *   q1, q2 [B][H][seq_q][d], k1, k2 [B][H][seq_k][d]: one byte per element,
+ *     OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *     subnormals; no infinities; codes 0x7f and 0xff are NaN), each tensor
+ *     with one scale: element = qk_scales[t] * decoded code;
+ *   qk_scales: HOST array of 4 fp32 scales (q1, q2, k1, k2), finite and > 0;
+ *   v [B][H][seq_k][dv] and out [B][H][seq_q][dv] bf16; lambda, lambda_init,
+ *     causal, dims->eps and dims->flags as diffattn_fwd.
+ * Each score is the exact sum of products of the codes (fp32 accumulation)
+ * times qk_scales[q] * qk_scales[k] / sqrt(d); the rest of the operator runs
+ * as in the bf16 prefill.  Supported: dims->dtype == DIFFATTN_BF16 (the type
+ * of v and out) with (head_dim, v_dim) = (64, 128); anything else returns
+ * DIFFATTN_ERR_UNSUPPORTED.  Quantising Q and K (choosing the scales,
+ * rounding to E4M3) is the caller's.
+ * Allocates nothing.  Returns a DIFFATTN_* status.
+ */
+int diffattn_fwd_fp8(const void* q1, const void* q2, const void* k1, const void* k2,
+                     const void* v, const float* qk_scales, const float* lambda,
+                     float lambda_init, int causal, void* out, const diffattn_dims* dims,
+                     void* stream);
+
+/*
  * Training forward: diffattn_fwd plus what diffattn_bwd needs, for bf16 with
  * (head_dim, v_dim) = (32, 64) or (64, 128) (else DIFFATTN_ERR_UNSUPPORTED).
  * The backward differentiates the same operator: lambda is a learnable scalar

@@ -314,3 +314,29 @@ def test_full_size_decode_sampled():
         assert_close(out[b:b + 1, h:h + 1], ref, torch.bfloat16, f"decode b{b} h{h}")
     del xg
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# key ranges past 2 GiB per (batch, head): per-tile buffer descriptors
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,dv,nk", [(64, 128, 8_400_013), (32, 64, 16_800_029)])
+def test_prefill_keys_past_2gib_per_head(d, dv, nk):
+    """V of one (batch, head) spans more than 2 GiB, so the kernel builds a
+    descriptor per tile instead of one per tensor; sampled rows of a
+    non-causal prefill over ~8.4M (or ~16.8M) keys with a ragged tail."""
+    assert nk * dv * 2 + 64 * 1024 >= 2 ** 31
+    w = _custom(1, 1, 40, nk, d, dv, "bf16", False, seed=97)
+    xg = workloads.make_prefill(w, device=DEV)
+    out = da.fwd(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"],
+                 lambda_init=w.lambda_init, causal=False, eps=w.eps)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    x = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in xg.items()}
+    del xg
+    torch.cuda.empty_cache()
+    rows = [0, 17, 39]
+    ref = oracle.head_rows(x["q1"][0, 0], x["q2"][0, 0], x["k1"][0, 0], x["k2"][0, 0],
+                           x["v"][0, 0], rows, causal=False, lam=float(x["lam"][0]),
+                           lambda_init=w.lambda_init, eps=w.eps)
+    assert_close(out[0, 0, rows], ref, torch.bfloat16, f"nk={nk}")

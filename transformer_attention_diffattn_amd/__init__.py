@@ -25,8 +25,9 @@ from typing import Optional, Sequence, Union
 import torch
 
 __all__ = [
-    "fwd", "decode", "decode_workspace_size", "decode_default_splits", "abi_version",
-    "library_path", "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
+    "fwd", "fwd_fp8", "fwd_train", "bwd", "bwd_workspace_size", "diag", "decode",
+    "decode_workspace_size", "decode_default_splits", "abi_version", "library_path",
+    "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +85,9 @@ def lib():
         L.diffattn_decode_default_splits.argtypes = [DP]
         L.diffattn_decode_workspace_size.restype = ctypes.c_size_t
         L.diffattn_decode_workspace_size.argtypes = [DP, ctypes.c_int32]
+        L.diffattn_fwd_fp8.restype = I
+        L.diffattn_fwd_fp8.argtypes = [P, P, P, P, P, ctypes.POINTER(ctypes.c_float), P, F, I, P,
+                                       DP, P]
         L.diffattn_fwd_train.restype = I
         L.diffattn_fwd_train.argtypes = [P, P, P, P, P, P, F, I, P, P, P, DP, P]
         L.diffattn_bwd_workspace_size.restype = ctypes.c_size_t
@@ -175,6 +179,46 @@ def fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
     st = lib().diffattn_fwd(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
                             v.data_ptr(), lam_t.data_ptr(), float(lambda_init), int(bool(causal)),
                             out.data_ptr(), ctypes.byref(dims), _stream_ptr(q1.device))
+    _check(st)
+    return out
+
+
+def fwd_fp8(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
+            v: torch.Tensor, qk_scales: Sequence[float],
+            lam: Union[float, Sequence[float], torch.Tensor], lambda_init: float = 0.8,
+            causal: bool = True, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+            pre_norm: bool = False) -> torch.Tensor:
+    """Prefill with e4m3 queries and keys: q1, q2, k1, k2 are
+    torch.float8_e4m3fn (or uint8 codes) [B,H,N,64], v bf16 [B,H,Nk,128];
+    qk_scales the four per-tensor dequantisation scales (q1, q2, k1, k2).
+    Returns out [B,H,Nq,128] bf16."""
+    qs = (q1, q2, k1, k2)
+    _require(all(t.dtype in (torch.float8_e4m3fn, torch.uint8) for t in qs),
+             "q1, q2, k1, k2 must be float8_e4m3fn (or uint8 codes)")
+    _require(v.dtype == torch.bfloat16, "v must be bfloat16")
+    ts = qs + (v,)
+    _require(all(t.is_cuda for t in ts), "inputs must be GPU tensors")
+    _require(all(t.device == q1.device for t in ts), "inputs must share one device")
+    _require(all(t.dim() == 4 for t in ts), "inputs must be [B,H,N,dim]")
+    _require(all(t.is_contiguous() for t in ts), "inputs must be contiguous")
+    B, H, Nq, d = q1.shape
+    Nk, dv = k1.shape[2], v.shape[3]
+    _require(q2.shape == (B, H, Nq, d), "q2 shape must equal q1 shape")
+    _require(k1.shape == (B, H, Nk, d) and k2.shape == (B, H, Nk, d), "k1/k2 shape mismatch")
+    _require(v.shape == (B, H, Nk, dv), "v shape mismatch")
+    sc = [float(x) for x in qk_scales]
+    _require(len(sc) == 4, "qk_scales must hold 4 values (q1, q2, k1, k2)")
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=torch.bfloat16, device=q1.device)
+    _require(out.shape == (B, H, Nq, dv) and out.dtype == torch.bfloat16 and out.is_contiguous()
+             and out.device == q1.device, "out must be a contiguous bf16 [B,H,Nq,dv] tensor")
+    lam_t = _lam_tensor(lam, H, q1.device)
+    dims = Dims(B, H, Nq, Nk, d, dv, BF16, float(eps), FLAG_PRE_NORM if pre_norm else 0)
+    scales = (ctypes.c_float * 4)(*sc)
+    st = lib().diffattn_fwd_fp8(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
+                                v.data_ptr(), scales, lam_t.data_ptr(), float(lambda_init),
+                                int(bool(causal)), out.data_ptr(), ctypes.byref(dims),
+                                _stream_ptr(q1.device))
     _check(st)
     return out
 

@@ -151,6 +151,49 @@ int diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
     return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
 }
 
+int diffattn_fwd_fp8(const void* q1, const void* q2, const void* k1, const void* k2,
+                     const void* v, const float* qk_scales, const float* lambda,
+                     float lambda_init, int causal, void* out, const diffattn_dims* dims,
+                     void* stream) {
+    int st = check_dims(dims);
+    if (st != DIFFATTN_OK) return st;
+    const void* ptrs[] = {q1, q2, k1, k2, v, lambda, out};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return DIFFATTN_ERR_INVALID;
+    if (!qk_scales || !isfinite(lambda_init)) return DIFFATTN_ERR_INVALID;
+    for (int i = 0; i < 4; ++i)
+        if (!(qk_scales[i] > 0.f) || !isfinite(qk_scales[i])) return DIFFATTN_ERR_INVALID;
+    const float s1 = qk_scales[0] * qk_scales[2], s2 = qk_scales[1] * qk_scales[3];
+    if (!(s1 > 0.f) || !isfinite(s1) || !(s2 > 0.f) || !isfinite(s2)) return DIFFATTN_ERR_INVALID;
+    if (dims->dtype != DIFFATTN_BF16 || dims->head_dim != 64 || dims->v_dim != 128)
+        return DIFFATTN_ERR_UNSUPPORTED;
+    if (causal && dims->seq_q != dims->seq_k) return DIFFATTN_ERR_UNSUPPORTED;
+
+    PrefillArgs a;
+    a.q1 = q1;
+    a.q2 = q2;
+    a.k1 = k1;
+    a.k2 = k2;
+    a.v = v;
+    a.lam = lambda;
+    a.out = out;
+    a.B = dims->batch;
+    a.H = dims->heads;
+    a.Nq = dims->seq_q;
+    a.Nk = dims->seq_k;
+    a.lambda_init = lambda_init;
+    a.eps = dims->eps;
+    a.scale_log2 = scale_log2(dims->head_dim);
+    a.flags = dims->flags;
+    a.d_save = nullptr;
+    a.lse = nullptr;
+    a.qk_scale[0] = s1;
+    a.qk_scale[1] = s2;
+    const hipError_t e = launch_prefill_fp8qk(a, dims->head_dim, dims->v_dim, causal != 0,
+                                              (hipStream_t)stream);
+    return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
+}
+
 // The training pair (forward that saves D and the log-sum-exp, backward):
 // bf16 with (d, dv) = (32, 64) or (64, 128).
 static int check_train_dims(const diffattn_dims* dims, int causal) {

@@ -27,6 +27,9 @@ struct PrefillArgs {
     // [2][B][H][Nq] fp32 (map 1, then map 2)
     float* d_save;
     float* lse;
+    // e4m3 Q/K variant only: per map, the product of the Q and K
+    // dequantisation scales (score = qk_scale[map] * sum of e4m3 products)
+    float qk_scale[2];
 };
 
 // Arguments of the backward kernels.  Pointers are device memory; layouts as
@@ -95,6 +98,9 @@ struct DecodeArgs {
 // the supported pairs; the callers have checked that.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
                                hipStream_t stream);
+// Q1, Q2, K1, K2 as OCP e4m3 bytes, V and the output bf16 (d = 64, dv = 128)
+hipError_t launch_prefill_fp8qk(const PrefillArgs& a, int d, int dv, bool causal,
+                                hipStream_t stream);
 hipError_t launch_prefill_bf16_wide(const PrefillArgs& a, int d, int dv, bool causal,
                                     hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,

@@ -74,7 +74,7 @@
 //   base + i of those 4 keys; two such reads give the 8 keys of a k-slot half.
 //
 // LDS per stage: K1, K2 and V tiles row-major without padding, 16-byte
-// chunks XOR-swizzled within each row (see k_swz, v_swz) so that operand
+// chunks XOR-swizzled within each row (see k_swz_rb, v_swz) so that operand
 // reads hit distinct banks.  Tiles are copied from global memory straight
 // into LDS by buffer loads with the LDS destination (no registers, no LDS
 // store instructions), through descriptors that end at the last key of the
@@ -99,6 +99,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 512;
@@ -107,20 +108,27 @@ constexpr int kBc = 32;                 // keys per tile
 constexpr float kSumLimit = 4096.0f;    // lazy-maximum bound on a lane's partial tile sum
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer descriptor word 3 for gfx9 parts
 
-template <int D, int DV>
+// F8: Q1, Q2, K1, K2 are e4m3 bytes (per-tensor scales in PrefillArgs), V bf16
+template <int D, int DV, bool F8 = false>
 struct Cfg {
     static constexpr int kBr = kBlocks * 32;
     static constexpr int kStages = 8;                      // LDS ring (a power of two)
     static constexpr int kAhead = 6;                       // tiles loaded ahead of use
-    static constexpr int kKElems = kBc * D;
+    static constexpr int kKRow = F8 ? D : 2 * D;           // bytes per K row
+    static constexpr int kKElems = kBc * kKRow / 2;        // K tile, in 16-bit units
     static constexpr int kVElems = kBc * DV;
-    static constexpr int kStage = 2 * kKElems + kVElems;  // bf16 elements per stage
-    static constexpr int kKChunks = kBc * D / 8;           // 16-byte chunks per K tile
+    static constexpr int kStage = 2 * kKElems + kVElems;  // 16-bit units per stage
+    static constexpr int kKChunks = kBc * kKRow / 16;      // 16-byte chunks per K tile
     static constexpr int kVChunks = kBc * DV / 8;
     static constexpr int kChunks = 2 * kKChunks + kVChunks;
-    static constexpr int kLoads = kChunks / kThreads;      // load instructions per wave and tile
-    static_assert(kChunks % kThreads == 0, "tile must split evenly over the threads");
-    static_assert(kKChunks % 64 == 0, "K regions must start on a wave boundary");
+    static constexpr int kWaves = kThreads / 64;
+    // load instructions per wave and tile: bf16, 16-byte loads spread evenly;
+    // e4m3, one 16-byte load of V and two 4-byte loads of K (K1 then K2)
+    static constexpr int kLoads = F8 ? 3 : kChunks / 64 / kWaves;
+    static_assert(F8 || kChunks % (64 * kWaves) == 0, "tile must split evenly over the waves");
+    static_assert(F8 || kKChunks % 64 == 0, "K regions must start on an instruction boundary");
+    static_assert(!F8 || (kVChunks == 64 * kWaves && kKChunks * 16 == 256 * kWaves),
+                  "e4m3 tile: one V load and one K1 and one K2 load per wave");
     // a stage is refilled kStages - kAhead tiles after the barrier that ends
     // its last reads (V of tile t is read in iteration t + 1)
     static_assert(kAhead + 2 <= kStages, "ring too small for the load distance");
@@ -148,13 +156,15 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 // read.  A K operand read gives 16 lanes 16 different rows at one chunk
 // column; a transposing V read gives 32 lanes 4 consecutive rows at one
 // 64-byte column.  The swizzles make those land on distinct banks.
-template <int D>
-__device__ __forceinline__ int k_swz(int r) {
-    if constexpr (D == 64)
+// swizzle of a K row's 16-byte chunks, by row length in bytes
+template <int RB>
+__device__ __forceinline__ int k_swz_rb(int r) {
+    if constexpr (RB == 128)
         return (r >> 1) & 7;  // 8 chunks per row, two rows per 256 bytes
     else
         return (r >> 2) & 3;  // 4 chunks per row, four rows per 256 bytes
 }
+
 template <int DV>
 __device__ __forceinline__ int v_swz(int r) {
     if constexpr (DV == 128)
@@ -224,11 +234,14 @@ __device__ __forceinline__ void prob_pair(const f32x16& s, int e, float sl2, flo
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
-template <int D, int DV, bool CAUSAL, bool FLAT>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
-    using C = Cfg<D, DV>;
+// The whole kernel; F8: Q1, Q2, K1, K2 are e4m3 codes (d = 64 only).
+template <int D, int DV, bool CAUSAL, bool FLAT, bool F8>
+__device__ __forceinline__ void prefill_items(PrefillArgs a) {
+    using C = Cfg<D, DV, F8>;
+    static_assert(!F8 || D == 64, "the e4m3 variant is for head_dim 64");
     constexpr int NDB = DV / 32;
-    constexpr int NKB = D / 16;
+    constexpr int NKB = D / 16;               // bf16 score products (k = 16 each)
+    constexpr int NKS = F8 ? D / 64 : NKB;    // score products of the variant in use
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::kSmemElems];
 
 
@@ -264,9 +277,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     const int h = bh % a.H;
     const float lam_h = a.lam[h];
 
-    const uint16_t* gq = (const uint16_t*)(map ? a.q2 : a.q1) + (size_t)bh * a.Nq * D;
-    const uint16_t* gk1 = (const uint16_t*)a.k1 + (size_t)bh * a.Nk * D;
-    const uint16_t* gk2 = (const uint16_t*)a.k2 + (size_t)bh * a.Nk * D;
+    constexpr int kQRow = F8 ? D : 2 * D;  // bytes per Q (and K) row
+    const char* gq = (const char*)(map ? a.q2 : a.q1) + (size_t)bh * a.Nq * kQRow;
+    const char* gk1 = (const char*)a.k1 + (size_t)bh * a.Nk * C::kKRow;
+    const char* gk2 = (const char*)a.k2 + (size_t)bh * a.Nk * C::kKRow;
     const uint16_t* gv = (const uint16_t*)a.v + (size_t)bh * a.Nk * DV;
     __bf16* gout = (__bf16*)a.out + (size_t)bh * a.Nq * DV;
 
@@ -274,12 +288,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     const int qrow = wq0 + l32;             // this lane's query row
 
     // Q fragments of the wave's map as B operands: column = query,
-    // k-slots = channels 16kb + 8lh ..
-    bf16x8 qf[NKB];
+    // k-slots = channels 16kb + 8lh .. (bf16), or bytes 32 lh .. 32 lh + 31
+    // of the row (e4m3: one k = 64 product covers d = 64)
+    bf16x8 qf[F8 ? 1 : NKB];
+    i32x8 qf8 = i32x8{};
+    if constexpr (F8) {
+        if (qrow < a.Nq) qf8 = *(const i32x8*)(gq + (size_t)qrow * kQRow + 32 * lh);
+        qf[0] = bf16x8{};
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-        qf[kb] = qrow < a.Nq ? *(const bf16x8*)(gq + (size_t)qrow * D + 16 * kb + 8 * lh)
-                             : bf16x8{};
+        for (int kb = 0; kb < NKB; ++kb)
+            qf[kb] = qrow < a.Nq ? *(const bf16x8*)(gq + (size_t)qrow * kQRow + 2 * (16 * kb + 8 * lh))
+                                 : bf16x8{};
+    }
 
     const int nkt_all = (a.Nk + kBc - 1) / kBc;
     const int nkt = CAUSAL ? min(nkt_all, (qt * C::kBr + C::kBr + kBc - 1) / kBc) : nkt_all;
@@ -293,20 +314,50 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     // lane loads the global chunk that belongs at its position under the
     // swizzle.  Regions start on instruction boundaries, so an instruction
     // reads one tensor; its descriptor ends at the last key, and lanes past
-    // it write zeros.
+    // it write zeros.  With e4m3 K (64-byte rows) the K regions are 2 KB
+    // each, which does not split into whole 16-byte instructions per wave:
+    // there each wave loads one 1 KB group of V and 256 bytes of each K with
+    // buffer_load_dword ... lds (lane i writes 4 bytes at M0 + 4 i), so every
+    // wave issues the same three loads per tile.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // provably uniform copy
-    int ld_off[C::kLoads];  // per instruction: this lane's byte offset in the tile
+    // per instruction i of this wave: where its 64 lanes write in the stage
+    // (bytes, lane 0; lane l writes 16 l or, for 4-byte loads, 4 l further),
+    // which tensor it reads (0: K1, 1: K2, 2: V), and this lane's byte
+    // offset in the tile of that tensor
+    uint32_t m0_off[C::kLoads];
+    int src[C::kLoads], ld_off[C::kLoads];
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-        const int c0 = 64 * (wave_u + i * (kThreads / 64));
-        if (c0 < 2 * C::kKChunks) {
-            const int pos = (c0 < C::kKChunks ? c0 : c0 - C::kKChunks) + lane;
-            const int row = pos / (D / 8);
-            ld_off[i] = row * D * 2 + 16 * ((pos % (D / 8)) ^ k_swz<D>(row));
+        if constexpr (F8) {
+            if (i == 0) {  // V: chunk group wave_u
+                const int c0 = 2 * C::kKChunks + 64 * wave_u;
+                const int pos = 64 * wave_u + lane;
+                const int row = pos / (DV / 8);
+                m0_off[i] = 16u * (uint32_t)c0;
+                src[i] = 2;
+                ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz<DV>(row));
+            } else {  // K1 (i = 1) or K2 (i = 2): 256 bytes, rows 4 wave_u ..
+                const int row = 4 * wave_u + (lane >> 4);
+                const int cp = (lane & 15) >> 2;  // chunk position in the row
+                m0_off[i] = (uint32_t)((i - 1) * C::kKChunks * 16 + 256 * wave_u);
+                src[i] = i - 1;
+                ld_off[i] = row * C::kKRow + 16 * (cp ^ k_swz_rb<C::kKRow>(row)) + 4 * (lane & 3);
+            }
         } else {
-            const int pos = c0 - 2 * C::kKChunks + lane;
-            const int row = pos / (DV / 8);
-            ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz<DV>(row));
+            const int c0 = 64 * (wave_u + i * (kThreads / 64));
+            m0_off[i] = 16u * (uint32_t)c0;
+            if (c0 < 2 * C::kKChunks) {
+                constexpr int kCpr = C::kKRow / 16;  // chunks per K row
+                const int pos = (c0 < C::kKChunks ? c0 : c0 - C::kKChunks) + lane;
+                const int row = pos / kCpr;
+                src[i] = c0 < C::kKChunks ? 0 : 1;
+                ld_off[i] = row * C::kKRow + 16 * ((pos % kCpr) ^ k_swz_rb<C::kKRow>(row));
+            } else {
+                const int pos = c0 - 2 * C::kKChunks + lane;
+                const int row = pos / (DV / 8);
+                src[i] = 2;
+                ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz<DV>(row));
+            }
         }
     }
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;  // LDS byte address
@@ -318,41 +369,49 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     uint32_t tile_bytes[C::kLoads], region_bytes[C::kLoads];
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-        const int c0 = 64 * (wave_u + i * (kThreads / 64));
-        const bool in_k = c0 < 2 * C::kKChunks;
-        const uint16_t* base = in_k ? (c0 < C::kKChunks ? gk1 : gk2) : gv;
-        const int64_t bytes = (int64_t)a.Nk * (in_k ? D : DV) * 2;
+        const bool in_k = src[i] < 2;
+        const void* base = in_k ? (const void*)(src[i] == 0 ? gk1 : gk2) : (const void*)gv;
+        const int row_bytes = in_k ? C::kKRow : DV * 2;
+        const int64_t bytes = (int64_t)a.Nk * row_bytes;
         rs[i] = sgpr_rsrc(base, bytes);
-        tile_bytes[i] = kBc * (in_k ? D : DV) * 2;
+        tile_bytes[i] = kBc * row_bytes;
         region_bytes[i] = FLAT ? (uint32_t)bytes : 0u;
     }
     auto issue_tile = [&](int kt) {
         const uint32_t stage = smem_base + 2u * (uint32_t)(stage_of(kt) * C::kStage);
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
-            const int c0 = 64 * (wave_u + i * (kThreads / 64));
-            const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + 16u * (uint32_t)c0);
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + m0_off[i]);
+            const bool dw = F8 && i > 0;  // 4-byte load
             // Tiles past this workgroup's last one read out of range: the
             // instruction count per tile stays fixed (the waits count on it)
             // and the lanes just write zeros, without touching memory.
+            int voff;
+            i32x4 rsrc;
             if constexpr (FLAT) {
                 const uint32_t toff = kt < nkt ? (uint32_t)kt * tile_bytes[i] : region_bytes[i];
-                asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                             :
-                             : "s"(m0), "v"(ld_off[i] + toff), "s"(rs[i])
-                             : "memory", "m0");
+                voff = ld_off[i] + (int)toff;
+                rsrc = rs[i];
             } else {
                 const int64_t key0 = (int64_t)kt * kBc;
                 const int64_t left = kt < nkt ? (int64_t)a.Nk - key0 : 0;
-                const bool in_k = c0 < 2 * C::kKChunks;
-                const uint16_t* base =
-                    in_k ? (c0 < C::kKChunks ? gk1 : gk2) + key0 * D : gv + key0 * DV;
-                const i32x4 rsrc = sgpr_rsrc(base, left * (in_k ? D : DV) * 2);
+                const bool in_k = src[i] < 2;
+                const int row_bytes = in_k ? C::kKRow : DV * 2;
+                const void* base = in_k ? (const void*)((src[i] == 0 ? gk1 : gk2) + key0 * C::kKRow)
+                                        : (const void*)(gv + key0 * DV);
+                voff = ld_off[i];
+                rsrc = sgpr_rsrc(base, left * row_bytes);
+            }
+            if (dw)
+                asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                             :
+                             : "s"(m0), "v"(voff), "s"(rsrc)
+                             : "memory", "m0");
+            else
                 asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                              :
-                             : "s"(m0), "v"(ld_off[i]), "s"(rsrc)
+                             : "s"(m0), "v"(voff), "s"(rsrc)
                              : "memory", "m0");
-            }
         }
     };
     // The loads above are invisible to the compiler's counters: before the
@@ -362,22 +421,40 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         constexpr int N = decltype(n)::value;
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
     };
+    // at most T tiles' loads of this wave in flight
+    auto wait_tiles = [&](auto t) {
+        constexpr int T = decltype(t)::value;
+        wait_loads(std::integral_constant<int, T * C::kLoads>{});
+    };
 
     const int krow = swap23(l32);
     // this lane's pieces of the wave's K tile (A operand): row krow, chunk
     // 2 kb + lh under the swizzle, in bf16 elements from the stage start
-    int k_off[NKB];
+    // (e4m3: bytes 32 lh .. 32 lh + 31 of the row, chunks 2 lh and 2 lh + 1)
+    int k_off[F8 ? 2 : NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-        k_off[kb] = map * C::kKElems + krow * D + 8 * ((2 * kb + lh) ^ k_swz<D>(krow));
+    for (int kb = 0; kb < (F8 ? 2 : NKB); ++kb)
+        k_off[kb] = map * C::kKElems + krow * (C::kKRow / 2) +
+                    8 * ((F8 ? 2 * lh + kb : 2 * kb + lh) ^ k_swz_rb<C::kKRow>(krow));
     auto k_operand = [&](int buf, int kb) {
         return *(const bf16x8*)(smem + buf * C::kStage + k_off[kb]);
+    };
+    // one score product: bf16 k = 16 step kb, or the whole e4m3 row (k = 64)
+    auto score_mfma = [&](int buf, int kb, f32x16 c) {
+        if constexpr (F8) {
+            const bf16x8 lo = k_operand(buf, 0), hi = k_operand(buf, 1);
+            const i32x8 ka8 = __builtin_bit_cast(
+                i32x8, __builtin_shufflevector(__builtin_bit_cast(i32x4, lo),
+                                               __builtin_bit_cast(i32x4, hi), 0, 1, 2, 3, 4, 5, 6, 7));
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka8, qf8, c, 0, 0, 0, 127, 0, 127);
+        } else {
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(buf, kb), qf[kb], c, 0, 0, 0);
+        }
     };
     auto scores = [&](int buf, f32x16& s) {
         s = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(buf, kb), qf[kb], s, 0, 0, 0);
+        for (int kb = 0; kb < NKS; ++kb) s = score_mfma(buf, kb, s);
     };
 
     // keys past the end, and keys after the query under the causal mask, to -inf
@@ -397,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     // i.e. chunk 4 db + 2 (vg%2) + (lane%4)/2 and byte 8 (lane%2) in it
     const int vg = lane >> 4;
     const int ve = (lane & 15) >> 2;
-    const int v_lane_row = 2 * C::kKElems + (8 * (vg >> 1) + ve) * DV + 4 * (lane & 1);
+    const int v_lane_row = 2 * C::kKElems + (8 * (vg >> 1) + ve) * DV + 4 * (lane & 1);  // 16-bit units
     int v_off[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -411,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    const float sl2 = a.scale_log2;
+    const float sl2 = F8 ? a.scale_log2 * a.qk_scale[map] : a.scale_log2;
     float m, l = 0.f;
     f32x16 o[NDB];
 #pragma unroll
@@ -448,11 +525,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     // and 1, which the first iteration needs anyway, and the rest follow.
     issue_tile(0);
     issue_tile(1);
+    if constexpr (F8) {
+        asm volatile("" ::"v"(qf8));
+    } else {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(qf[kb]));
+        for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(qf[kb]));
+    }
 #pragma unroll
     for (int t0 = 2; t0 < C::kAhead; ++t0) issue_tile(t0);
-    wait_loads(std::integral_constant<int, (C::kAhead - 2) * C::kLoads>{});
+    wait_tiles(std::integral_constant<int, C::kAhead - 2>{});
     __syncthreads();
     scores(0, A.s);
     if (nfull < 1) mask(0, A.s);
@@ -474,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     //                        starting in a slot -1 that has no product; the
     //                        loads of tile j+6 early.
     constexpr int kPairsV = 2 * NDB;  // V operands (db, kb)
-    constexpr int kSlots = NKB + kPairsV;
+    constexpr int kSlots = NKS + kPairsV;
     constexpr int kLookahead = 3;
     constexpr int kLoadSlot = 1;
     // probability pair k (registers 2k, 2k+1) starts in slot pair_slot(k)
@@ -488,10 +569,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         constexpr bool NEXT = decltype(next)::value;
         const float base = m == -INFINITY ? 0.f : m;
 
-        bf16x8 ka[NKB], va[kPairsV];
+        bf16x8 ka[F8 ? 2 : NKB], va[kPairsV];
         if constexpr (NEXT) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) ka[kb] = k_operand(stage_of(j + 1), kb);
+            for (int kb = 0; kb < (F8 ? 2 : NKB); ++kb) ka[kb] = k_operand(stage_of(j + 1), kb);
         }
         const int vbuf = stage_of(j - 1);
         if constexpr (PREV) {
@@ -505,13 +586,26 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         for (int slot = -1; slot < kSlots; ++slot) {
             if (slot < 0) {
                 // no product: the first operands are still on their way
-            } else if (slot < NKB) {
-                if constexpr (NEXT)
-                    oth.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        ka[slot], qf[slot], slot == 0 ? f32x16{} : oth.s, 0, 0, 0);
+            } else if (slot < NKS) {
+                if constexpr (NEXT) {
+                    if constexpr (F8) {
+                        const i32x8 ka8 = __builtin_bit_cast(
+                            i32x8, __builtin_shufflevector(__builtin_bit_cast(i32x4, ka[0]),
+                                                           __builtin_bit_cast(i32x4, ka[1]), 0, 1,
+                                                           2, 3, 4, 5, 6, 7));
+                        oth.s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            ka8, qf8, f32x16{}, 0, 0, 0, 127, 0, 127);
+                        // keep it first: its result is the next iteration's
+                        // first input (the scheduler would sink it to the end)
+                        __builtin_amdgcn_sched_barrier(0);
+                    } else {
+                        oth.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            ka[slot], qf[slot], slot == 0 ? f32x16{} : oth.s, 0, 0, 0);
+                    }
+                }
             } else {
                 if constexpr (PREV) {
-                    const int q = slot - NKB;
+                    const int q = slot - NKS;
                     if (q + kLookahead < kPairsV)
                         va[q + kLookahead] =
                             v_operand(vbuf, (q + kLookahead) >> 1, (q + kLookahead) & 1);
@@ -563,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         l += tsum;
         // tile j+2 (read from the next iteration on) must have landed; tiles
         // j+3 .. j+kAhead may still be in flight
-        wait_loads(std::integral_constant<int, (C::kAhead - 2) * C::kLoads>{});
+        wait_tiles(std::integral_constant<int, C::kAhead - 2>{});
         __syncthreads();
     };
 
@@ -601,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     const float L = l + xor32(l);
     // every wave is done with the tile ring, and no load (the last ones read
     // past the end and write zeros) may land on the epilogue's areas
-    wait_loads(std::integral_constant<int, 0>{});
+    wait_tiles(std::integral_constant<int, 0>{});
     __syncthreads();
     const int other = map ^ 1;
     const float cs = map ? lam_h / L : 1.f / L;
@@ -717,9 +811,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     }
 }
 
-template <int D, int DV>
+template <int D, int DV, bool CAUSAL, bool FLAT>
+__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
+    prefill_items<D, DV, CAUSAL, FLAT, false>(a);
+}
+
+// Scores from e4m3 queries and keys (per-tensor scales in a.qk_scale).
+template <bool CAUSAL, bool FLAT>
+__global__ __launch_bounds__(kThreads) void prefill_fp8qk_kernel(PrefillArgs a) {
+    prefill_items<64, 128, CAUSAL, FLAT, true>(a);
+}
+
+template <int D, int DV, bool F8>
 hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
-    const int nqt = (a.Nq + Cfg<D, DV>::kBr - 1) / Cfg<D, DV>::kBr;
+    const int nqt = (a.Nq + Cfg<D, DV, F8>::kBr - 1) / Cfg<D, DV, F8>::kBr;
     const int64_t items = (int64_t)nqt * a.B * a.H;
     // item indices (and the snake's r * G + w) stay in int range
     if (items > (int64_t)0x7fffffff - 4096) return hipErrorInvalidValue;
@@ -729,10 +834,17 @@ hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
     void* args[] = {&copy};
     // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
     const bool flat = (int64_t)a.Nk * DV * 2 + 64 * 1024 < (int64_t)0x7fffffff;
-    const void* fn = causal ? (flat ? (const void*)prefill_bf16_kernel<D, DV, true, true>
-                                    : (const void*)prefill_bf16_kernel<D, DV, true, false>)
-                            : (flat ? (const void*)prefill_bf16_kernel<D, DV, false, true>
-                                    : (const void*)prefill_bf16_kernel<D, DV, false, false>);
+    const void* fn;
+    if constexpr (F8)
+        fn = causal ? (flat ? (const void*)prefill_fp8qk_kernel<true, true>
+                            : (const void*)prefill_fp8qk_kernel<true, false>)
+                    : (flat ? (const void*)prefill_fp8qk_kernel<false, true>
+                            : (const void*)prefill_fp8qk_kernel<false, false>);
+    else
+        fn = causal ? (flat ? (const void*)prefill_bf16_kernel<D, DV, true, true>
+                            : (const void*)prefill_bf16_kernel<D, DV, true, false>)
+                    : (flat ? (const void*)prefill_bf16_kernel<D, DV, false, true>
+                            : (const void*)prefill_bf16_kernel<D, DV, false, false>);
     return hipLaunchKernel(fn, grid, dim3(kThreads), args, 0, stream);
 }
 
@@ -740,9 +852,15 @@ hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
                                hipStream_t stream) {
-    if (d == 32 && dv == 64) return launch_dims<32, 64>(a, causal, stream);
-    if (d == 64 && dv == 128) return launch_dims<64, 128>(a, causal, stream);
+    if (d == 32 && dv == 64) return launch_dims<32, 64, false>(a, causal, stream);
+    if (d == 64 && dv == 128) return launch_dims<64, 128, false>(a, causal, stream);
     if (d == 128 && dv == 256) return launch_prefill_bf16_wide(a, d, dv, causal, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_fp8qk(const PrefillArgs& a, int d, int dv, bool causal,
+                                hipStream_t stream) {
+    if (d == 64 && dv == 128) return launch_dims<64, 128, true>(a, causal, stream);
     return hipErrorInvalidValue;
 }
 
