@@ -39,7 +39,9 @@ CSRC = os.path.join(ROOT, "transformer_attention_diffattn_amd", "csrc")
 # the trace pass runs the default benchmark command itself, so that its
 # average launch durations are those of the reported figures
 BENCH_ARGS: list = []
-PMC_BENCH_ARGS = ["--steps", "3", "--warmup", "1", "--no-cpu", "--copy-calibration"]
+# the counter passes need only the headline prefill and the decode launches
+PMC_BENCH_ARGS = ["--steps", "3", "--warmup", "1", "--no-cpu", "--no-backward", "--no-diag",
+                  "--no-fp8", "--copy-calibration"]
 COPY_BYTES = 1 << 30
 COPY_GRID = COPY_BYTES // 16  # threads of the vectorised copy (4 floats per thread)
 
@@ -233,7 +235,8 @@ def _counter_cmd(out: str, i: int, workload: str):
     py = sys.executable or "python3"
     return ["rocprofv3", "--pmc", *COUNTER_PASSES[i], "-d", os.path.join(out, f"counters{i}"),
             "-o", "run", "-f", "csv", "--", py, os.path.join(ROOT, "bench.py"), "--steps", "3",
-            "--warmup", "1", "--no-cpu", "--no-decode", "--workload", workload]
+            "--warmup", "1", "--no-cpu", "--no-decode", "--no-backward", "--no-diag", "--no-fp8",
+            "--workload", workload]
 
 
 def prefill_kernel_of(workload: str) -> str:

@@ -234,8 +234,9 @@ __device__ __forceinline__ void prob_pair(const f32x16& s, int e, float sl2, flo
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
-// The whole kernel; F8: Q1, Q2, K1, K2 are e4m3 codes (d = 64 only).
-template <int D, int DV, bool CAUSAL, bool FLAT, bool F8>
+// The whole kernel; F8: Q1, Q2, K1, K2 are e4m3 codes (d = 64 only);
+// SAVE: also write D and the log-sum-exp rows for the backward.
+template <int D, int DV, bool CAUSAL, bool FLAT, bool F8, bool SAVE>
 __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     using C = Cfg<D, DV, F8>;
     static_assert(!F8 || D == 64, "the e4m3 variant is for head_dim 64");
@@ -724,7 +725,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
             }
         }
     }
-    if (a.lse) {
+    if constexpr (SAVE) {
         // training forward: D before the normalisation, and each map's
         // log-sum-exp (m and l share the lazy maximum, so m + log2 l is exact)
         if (qrow < a.Nq) {
@@ -813,13 +814,19 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
 
 template <int D, int DV, bool CAUSAL, bool FLAT>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
-    prefill_items<D, DV, CAUSAL, FLAT, false>(a);
+    prefill_items<D, DV, CAUSAL, FLAT, false, false>(a);
+}
+
+// The training forward: the same, plus a.d_save and a.lse.
+template <int D, int DV, bool CAUSAL, bool FLAT>
+__global__ __launch_bounds__(kThreads) void prefill_train_kernel(PrefillArgs a) {
+    prefill_items<D, DV, CAUSAL, FLAT, false, true>(a);
 }
 
 // Scores from e4m3 queries and keys (per-tensor scales in a.qk_scale).
 template <bool CAUSAL, bool FLAT>
 __global__ __launch_bounds__(kThreads) void prefill_fp8qk_kernel(PrefillArgs a) {
-    prefill_items<64, 128, CAUSAL, FLAT, true>(a);
+    prefill_items<64, 128, CAUSAL, FLAT, true, false>(a);
 }
 
 template <int D, int DV, bool F8>
@@ -840,6 +847,11 @@ hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
                             : (const void*)prefill_fp8qk_kernel<true, false>)
                     : (flat ? (const void*)prefill_fp8qk_kernel<false, true>
                             : (const void*)prefill_fp8qk_kernel<false, false>);
+    else if (a.lse)
+        fn = causal ? (flat ? (const void*)prefill_train_kernel<D, DV, true, true>
+                            : (const void*)prefill_train_kernel<D, DV, true, false>)
+                    : (flat ? (const void*)prefill_train_kernel<D, DV, false, true>
+                            : (const void*)prefill_train_kernel<D, DV, false, false>);
     else
         fn = causal ? (flat ? (const void*)prefill_bf16_kernel<D, DV, true, true>
                             : (const void*)prefill_bf16_kernel<D, DV, true, false>)
