@@ -35,7 +35,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "get", "make_prefill", "make_decode", "make", "needle_plan",
-           "quantize_e4m3", "make_prefill_fp8"]
+           "quantize_e4m3", "make_prefill_fp8", "make_proj"]
 
 
 @dataclass(frozen=True)
@@ -347,3 +347,25 @@ def make_prefill_fp8(w: Workload, device: str | torch.device = "cpu", seed: Opti
         scales.append(s)
     x["scales"] = scales
     return x
+
+
+# --------------------------------------------------------------------------
+# inputs of the Q/K/V projection
+# --------------------------------------------------------------------------
+
+def make_proj(w: Workload, d_model: Optional[int] = None, device: str | torch.device = "cpu",
+              seed: Optional[int] = None):
+    """Hidden states and projection weight for workload w's attention shapes:
+    x [B][N][d_model] ~ N(0, 1) and wt [H (4 d + dv)][d_model] ~ N(0, 1/d_model)
+    (unit-variance outputs), both in w's storage dtype.  d_model defaults to
+    H dv.  One torch.Generator seeded with the workload's seed (plus 1000) on
+    ``device`` draws x, then wt."""
+    dm = d_model if d_model is not None else w.H * w.dv
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(w.seed if seed is None else seed) + 1000)
+    dt = w.torch_dtype
+    x = torch.randn((w.B, w.nq, dm), generator=g, device=dev, dtype=torch.float32).to(dt)
+    wt = torch.randn((w.H * (4 * w.d + w.dv), dm), generator=g, device=dev, dtype=torch.float32)
+    wt = wt.mul_(1.0 / math.sqrt(dm)).to(dt)
+    return {"x": x, "w": wt, "d_model": dm}
