@@ -121,6 +121,28 @@ int diffattn_fwd_fp8(const void* q1, const void* q2, const void* k1, const void*
                      void* stream);
 
 /*
+ * The projections in front of the operator, fused with the split into heads
+ * (step 1 on llmbytes.dev, "How Differential Attention Cancels Common-Mode
+ * Noise": per head, two queries, two keys and one value projected from the
+ * input): Y = X W^T in one pass, written straight into the layout the other
+ * entry points read.
+ *   x [batch][seq][model_dim] bf16 (hidden states, tokens in order);
+ *   w [heads * (4 head_dim + v_dim)][model_dim] bf16, a linear layer's
+ *     (output feature, input feature) layout; output feature f belongs to
+ *     head h = f / S, S = 4 head_dim + v_dim, at offset o = f - h S, with
+ *     Q1 at o in [0, d), Q2 [d, 2d), K1 [2d, 3d), K2 [3d, 4d), V [4d, S);
+ *   q1, q2, k1, k2 [batch][heads][seq][head_dim], v [batch][heads][seq][v_dim]
+ *     bf16 (fp32 accumulation, one rounding to nearest even).
+ * Supported: (head_dim, v_dim) as diffattn_fwd; model_dim a multiple of 32,
+ * at most 2^20; batch * seq and the output feature count below 2^31 - 256.
+ * Outputs must not overlap the inputs or each other.  All pointers device
+ * memory, 16-byte aligned.  Allocates nothing.  Returns a DIFFATTN_* status.
+ */
+int diffattn_qkv_proj(const void* x, const void* w, int32_t batch, int32_t seq, int32_t heads,
+                      int32_t head_dim, int32_t v_dim, int32_t model_dim, void* q1, void* q2,
+                      void* k1, void* k2, void* v, void* stream);
+
+/*
  * Training forward: diffattn_fwd plus what diffattn_bwd needs, for bf16 with
  * (head_dim, v_dim) = (32, 64) or (64, 128) (else DIFFATTN_ERR_UNSUPPORTED).
  * The backward differentiates the same operator: lambda is a learnable scalar

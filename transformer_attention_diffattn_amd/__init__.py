@@ -25,7 +25,7 @@ from typing import Optional, Sequence, Union
 import torch
 
 __all__ = [
-    "fwd", "fwd_fp8", "fwd_train", "bwd", "bwd_workspace_size", "diag", "decode",
+    "fwd", "fwd_fp8", "fwd_train", "qkv_proj", "bwd", "bwd_workspace_size", "diag", "decode",
     "decode_workspace_size", "decode_default_splits", "abi_version", "library_path",
     "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
 ]
@@ -88,6 +88,9 @@ def lib():
         L.diffattn_fwd_fp8.restype = I
         L.diffattn_fwd_fp8.argtypes = [P, P, P, P, P, ctypes.POINTER(ctypes.c_float), P, F, I, P,
                                        DP, P]
+        i32 = ctypes.c_int32
+        L.diffattn_qkv_proj.restype = I
+        L.diffattn_qkv_proj.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P]
         L.diffattn_fwd_train.restype = I
         L.diffattn_fwd_train.argtypes = [P, P, P, P, P, P, F, I, P, P, P, DP, P]
         L.diffattn_bwd_workspace_size.restype = ctypes.c_size_t
@@ -221,6 +224,32 @@ def fwd_fp8(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tens
                                 _stream_ptr(q1.device))
     _check(st)
     return out
+
+
+def qkv_proj(x: torch.Tensor, w: torch.Tensor, heads: int, head_dim: int, v_dim: int,
+             out: Optional[Sequence[torch.Tensor]] = None):
+    """Fused projections: x [B,N,d_model] bf16, w [heads*(4 d + dv), d_model]
+    bf16 (per head the Q1, Q2, K1, K2, V output rows in that order).  Returns
+    (q1, q2, k1, k2, v) with q*, k* [B,H,N,d] and v [B,H,N,dv], ready for
+    ``fwd``."""
+    _require(x.is_cuda and w.is_cuda and x.device == w.device, "x and w must be on one GPU")
+    _require(x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16, "x and w must be bfloat16")
+    _require(x.dim() == 3 and w.dim() == 2, "x must be [B,N,d_model] and w [n_out,d_model]")
+    _require(x.is_contiguous() and w.is_contiguous(), "x and w must be contiguous")
+    B, N, dm = x.shape
+    H, d, dv = int(heads), int(head_dim), int(v_dim)
+    _require(w.shape == (H * (4 * d + dv), dm), "w must be [heads*(4 d + dv), d_model]")
+    shapes = [(B, H, N, d)] * 4 + [(B, H, N, dv)]
+    if out is None:
+        out = [torch.empty(s, dtype=torch.bfloat16, device=x.device) for s in shapes]
+    _require(len(out) == 5 and all(o.shape == s and o.dtype == torch.bfloat16
+                                   and o.is_contiguous() and o.device == x.device
+                                   for o, s in zip(out, shapes)),
+             "out must be five contiguous bf16 tensors of the output shapes")
+    st = lib().diffattn_qkv_proj(x.data_ptr(), w.data_ptr(), B, N, H, d, dv, dm,
+                                 *[o.data_ptr() for o in out], _stream_ptr(x.device))
+    _check(st)
+    return tuple(out)
 
 
 def _check_inputs(q1, q2, k1, k2, v):

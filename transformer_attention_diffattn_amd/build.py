@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libdiffattn.so")
-SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_bf16_wide.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "diag.hip"]
+SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_bf16_wide.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "diag.hip", "proj.hip"]
 # Per-source extra flags.  The narrow-head prefill kernel keeps its score
 # accumulators in ordinary VGPRs, where the softmax reads them without a copy
 # out of the accumulation registers; the compiler's default heuristic would

@@ -194,6 +194,38 @@ int diffattn_fwd_fp8(const void* q1, const void* q2, const void* k1, const void*
     return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
 }
 
+int diffattn_qkv_proj(const void* x, const void* w, int32_t batch, int32_t seq, int32_t heads,
+                      int32_t head_dim, int32_t v_dim, int32_t model_dim, void* q1, void* q2,
+                      void* k1, void* k2, void* v, void* stream) {
+    const void* ptrs[] = {x, w, q1, q2, k1, k2, v};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return DIFFATTN_ERR_INVALID;
+    if (batch < 1 || seq < 1 || heads < 1 || head_dim < 1 || v_dim < 1 || model_dim < 1)
+        return DIFFATTN_ERR_INVALID;
+    if (!supported_dims(head_dim, v_dim)) return DIFFATTN_ERR_UNSUPPORTED;
+    if (model_dim % 32 != 0 || model_dim > (1 << 20)) return DIFFATTN_ERR_UNSUPPORTED;
+    const int64_t T = (int64_t)batch * seq;
+    const int64_t n_out = (int64_t)heads * (4 * head_dim + v_dim);
+    if (T > 0x7fffffff - 256 || n_out > 0x7fffffff - 256) return DIFFATTN_ERR_UNSUPPORTED;
+    ProjArgs a;
+    a.x = x;
+    a.w = w;
+    a.q1 = q1;
+    a.q2 = q2;
+    a.k1 = k1;
+    a.k2 = k2;
+    a.v = v;
+    a.T = (int32_t)T;
+    a.N = seq;
+    a.H = heads;
+    a.d = head_dim;
+    a.dv = v_dim;
+    a.d_model = model_dim;
+    a.n_out = (int32_t)n_out;
+    const hipError_t e = launch_qkv_proj_bf16(a, (hipStream_t)stream);
+    return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
+}
+
 // The training pair (forward that saves D and the log-sum-exp, backward):
 // bf16 with (d, dv) = (32, 64) or (64, 128).
 static int check_train_dims(const diffattn_dims* dims, int causal) {

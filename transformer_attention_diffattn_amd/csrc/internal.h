@@ -32,6 +32,19 @@ struct PrefillArgs {
     float qk_scale[2];
 };
 
+// Arguments of the fused Q/K/V projection.  x [T][d_model] (T = B N tokens),
+// w [n_out][d_model] with n_out = H (4 d + dv); outputs head-major.
+struct ProjArgs {
+    const void* x;
+    const void* w;
+    void* q1;
+    void* q2;
+    void* k1;
+    void* k2;
+    void* v;
+    int32_t T, N, H, d, dv, d_model, n_out;
+};
+
 // Arguments of the backward kernels.  Pointers are device memory; layouts as
 // in diffattn.h.
 struct BackwardArgs {
@@ -101,6 +114,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
 // Q1, Q2, K1, K2 as OCP e4m3 bytes, V and the output bf16 (d = 64, dv = 128)
 hipError_t launch_prefill_fp8qk(const PrefillArgs& a, int d, int dv, bool causal,
                                 hipStream_t stream);
+hipError_t launch_qkv_proj_bf16(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16_wide(const PrefillArgs& a, int d, int dv, bool causal,
                                     hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
