@@ -19,7 +19,9 @@ recomputed, one shared dP, dV, dK1, dK2, dQ1, dQ2), runs the map
 diagnostics on the 32K needle workload ("diagnostics": the row-max sweep at
 4 d flops per unmasked pair, the needle weights, and the values they give on
 those synthetic inputs), times the prefill with Q and K quantised to E4M3
-("fp8_qk"), and times the fp64 CPU oracle on a bounded sample of
+("fp8_qk"), times the fused Q/K/V projection that produces the headline's
+inputs from d_model = H dv hidden states ("qkv_proj"), and times the fp64 CPU
+oracle on a bounded sample of
 the headline workload ("cpu_baseline").
 
 Prints one JSON line on stdout.
@@ -297,6 +299,42 @@ def bench_fp8(w, steps: int, warmup: int):
     return min(t8), min(t16)
 
 
+def bench_proj(w, steps: int, warmup: int):
+    """ms per diffattn_qkv_proj launch for workload w's attention shapes
+    (d_model = H dv), and ms per library GEMM (torch.matmul) of the same
+    operands without the head split, for context."""
+    import torch
+
+    import transformer_attention_diffattn_amd as da
+    import workloads
+
+    p = workloads.make_proj(w, device="cuda")
+    x, wt = p["x"], p["w"]
+    outs = [torch.empty(s, dtype=torch.bfloat16, device="cuda")
+            for s in [(w.B, w.H, w.nq, w.d)] * 4 + [(w.B, w.H, w.nq, w.dv)]]
+    y = torch.empty((w.B * w.nq, wt.shape[0]), dtype=torch.bfloat16, device="cuda")
+    x2 = x.reshape(w.B * w.nq, p["d_model"])
+
+    def step():
+        da.qkv_proj(x, wt, w.H, w.d, w.dv, out=outs)
+
+    def lib_step():
+        torch.matmul(x2, wt.t(), out=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = _events_time(step, steps)
+    for _ in range(max(2, warmup // 4)):
+        lib_step()
+    torch.cuda.synchronize()
+    lib_ms = _events_time(lib_step, steps)
+    flops = 2 * w.B * w.nq * p["d_model"] * wt.shape[0]
+    del p, x, wt, outs, y
+    torch.cuda.empty_cache()
+    return ms, lib_ms, flops
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +347,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-diag", action="store_true", help="skip the diagnostics leg")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 query/key leg")
+    ap.add_argument("--no-proj", action="store_true", help="skip the Q/K/V projection leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain fp32 copy of 1 GiB (3 times), the reference the "
                          "HBM byte counters are scaled by")
@@ -430,6 +469,21 @@ def main():
                          "achieved": round(ftf, 2), "peak": round(mix_peak, 1),
                          "unit": "TFLOP/s", "frac": round(ftf / mix_peak, 4),
                          "traffic": None},
+        }
+
+    if not args.no_proj and w.dtype == "bf16":
+        pms, lms, pflops = bench_proj(w, max(10, args.steps // 3), max(20, args.warmup // 3))
+        ptf = pflops / (pms * 1e-3) / 1e12
+        rec["qkv_proj"] = {
+            "workload": f"{w.name} projections (d_model {w.H * w.dv})",
+            "value": round(ptf, 2),
+            "unit": "TFLOP/s",
+            "ms_per_call": round(pms, 4),
+            "flops_per_call": pflops,
+            "library_gemm_ms_no_head_split": round(lms, 4),
+            "roofline": {"bound": "mfma", "kernel": "qkv_proj_kernel", "achieved": round(ptf, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ptf / PEAK_BF16_TFLOPS, 4), "traffic": None},
         }
 
     if not args.no_diag:

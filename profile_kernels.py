@@ -41,7 +41,7 @@ CSRC = os.path.join(ROOT, "transformer_attention_diffattn_amd", "csrc")
 BENCH_ARGS: list = []
 # the counter passes need only the headline prefill and the decode launches
 PMC_BENCH_ARGS = ["--steps", "3", "--warmup", "1", "--no-cpu", "--no-backward", "--no-diag",
-                  "--no-fp8", "--copy-calibration"]
+                  "--no-proj", "--no-fp8", "--copy-calibration"]
 COPY_BYTES = 1 << 30
 COPY_GRID = COPY_BYTES // 16  # threads of the vectorised copy (4 floats per thread)
 
@@ -236,7 +236,7 @@ def _counter_cmd(out: str, i: int, workload: str):
     return ["rocprofv3", "--pmc", *COUNTER_PASSES[i], "-d", os.path.join(out, f"counters{i}"),
             "-o", "run", "-f", "csv", "--", py, os.path.join(ROOT, "bench.py"), "--steps", "3",
             "--warmup", "1", "--no-cpu", "--no-decode", "--no-backward", "--no-diag", "--no-fp8",
-            "--workload", workload]
+            "--no-proj", "--workload", workload]
 
 
 def prefill_kernel_of(workload: str) -> str:

@@ -90,13 +90,11 @@ def test_proj_then_attention_matches_oracle_chain():
     lam = torch.tensor([0.3, 0.5, 0.7, 0.2], dtype=torch.float32)
     out = da.fwd(q1, q2, k1, k2, v, lam.cuda(), causal=True)
     torch.cuda.synchronize()
-    ref_p = oproj.qkv_proj(p["x"], p["w"], heads=H, head_dim=d, v_dim=dv)
-    # the forward oracle reads the bf16 projections the GPU produced, which
-    # the parity check above bounds against ref_p
+    # the projections against the projection oracle, then the forward oracle
+    # on the bf16 projections the GPU produced (what the forward read)
     _check((q1, q2, k1, k2, v), p["x"], p["w"], H, d, dv)
     ref = oracle.fwd(q1.cpu(), q2.cpu(), k1.cpu(), k2.cpu(), v.cpu(), lam, causal=True)
     assert_close(out, ref, torch.bfloat16, "projection then attention")
-    assert ref_p["q1"].shape == tuple(q1.shape)
 
 
 def test_proj_rejects_unsupported():

@@ -11,11 +11,13 @@
 //
 // Workgroup = 256 output features x 256 tokens, 8 waves (4 feature quarters
 // x 2 token halves), each 64 x 128 as 2 x 4 blocks of 32 x 32.  The
-// contraction runs in steps of 32: both tiles of a step (W and X rows, 64
-// bytes each) go from global memory straight into a 4-stage LDS ring by
-// buffer loads with the LDS destination, three steps ahead.  Rows are 64 bytes,
-// four per 256-byte bank line; chunk c of row r sits at c ^ ((r >> 2) & 3),
-// so the 16 rows a 16-byte operand read touches at once hit distinct banks.
+// contraction runs in steps of 64: both tiles of a step (W and X rows, 128
+// bytes each: whole cache lines) go from global memory straight into a
+// 2-stage LDS ring by buffer loads with the LDS destination, one step ahead.
+// Rows are 128 bytes, two per 256-byte bank line; chunk c of row r sits at
+// c ^ ((r >> 1) & 7), so the 16 rows a 16-byte operand read touches at once
+// hit distinct banks.  (Steps of 32 in a 4-stage ring, half cache lines per
+// row and step, measured 5% slower.)
 
 #include "internal.h"
 
@@ -34,8 +36,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 512;
 constexpr int kTileF = 256;   // output features per workgroup
 constexpr int kTileT = 256;   // tokens per workgroup
-constexpr int kStepK = 32;    // contraction elements per stage
-constexpr int kStages = 4;
+constexpr int kStepK = 64;    // contraction elements per stage
+constexpr int kStages = 2;
 constexpr int kAhead = kStages - 1;
 constexpr int kRowBytes = kStepK * 2;                       // 64
 constexpr int kRegionBytes = kTileF * kRowBytes;           // one operand's tile: 16 KB
@@ -44,9 +46,10 @@ constexpr int kLoads = kStageBytes / 16 / 64 / (kThreads / 64);  // per wave and
 constexpr int kGroupT = 4;    // token tiles per group of the tile order
 constexpr int kBufferWord3 = 0x00020000;
 static_assert(kTileF == kTileT, "the two regions share one load layout");
-static_assert(kLoads == 4, "two loads of each region per wave");
+static_assert(kLoads == 8, "four loads of each region per wave");
+constexpr int kCpr = kRowBytes / 16;
 
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ i32x4 rsrc(const void* base, int64_t bytes) {
     const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
@@ -86,11 +89,14 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_kernel(ProjArgs a) {
     const int f0 = tile_f * kTileF, t0 = tile_t * kTileT;
 
     const int64_t row_bytes = (int64_t)a.d_model * 2;
-    const int nst = a.d_model / kStepK;
+    // d_model is a multiple of 32: a last step of 32 uses its first half
+    // only (its second half reads past the row: the next row, or zeros)
+    const int nst = (a.d_model + kStepK - 1) / kStepK;
+    const int half_last = (a.d_model % kStepK) != 0 ? nst - 1 : -1;
 
-    // loads: instruction i of wave w fills LDS chunk positions 64 (w + 8 i) ..
-    // of the stage (W region for i < 2, X region for i >= 2); lane l takes
-    // row (64 j + l) / 4 of its region, chunk position (64 j + l) % 4
+    // loads: instruction i of wave w fills LDS chunk positions 64 j .. of its
+    // region (W for i < 4, X for i >= 4; j = w + 8 (i % 4)); lane l takes
+    // row (64 j + l) / 8 of the region, chunk position (64 j + l) % 8
     i32x4 rs[2];
     uint32_t region[2];
     {
@@ -103,11 +109,11 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_kernel(ProjArgs a) {
     uint32_t ld_off[kLoads], m0_off[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-        const int j = wave_u + (kThreads / 64) * (i & 1);  // instruction within the region
+        const int j = wave_u + (kThreads / 64) * (i & 3);  // instruction within the region
         const int pos = 64 * j + lane;
-        const int row = pos >> 2, cp = pos & 3;
+        const int row = pos / kCpr, cp = pos % kCpr;
         ld_off[i] = (uint32_t)(row * row_bytes) + 16u * (uint32_t)(cp ^ swz(row));
-        m0_off[i] = (uint32_t)((i >> 1) * kRegionBytes + 16 * 64 * j);
+        m0_off[i] = (uint32_t)((i >> 2) * kRegionBytes + 16 * 64 * j);
     }
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
     // stages past the last one read out of range (zeros, no memory touched),
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_kernel(ProjArgs a) {
         const uint32_t stage = smem_base + (uint32_t)((s & (kStages - 1)) * kStageBytes);
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            const int r = i >> 1;
+            const int r = i >> 2;
             const uint32_t toff = s < nst ? (uint32_t)s * kRowBytes : region[r];
             const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + m0_off[i]);
             asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -127,10 +133,10 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_kernel(ProjArgs a) {
     };
 
     // operand reads: A = W rows wf*64 + 32 fb + l32, B = X rows wt*128 + 32 tb
-    // + l32; k-step ks of a stage is chunk 2 ks + lh
-    int a_off[2][2], b_off[4][2];
+    // + l32; k-step ks (of 4) of a stage is chunk 2 ks + lh
+    int a_off[2][4], b_off[4][4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
             const int row = wf * 64 + 32 * fb + l32;
@@ -152,13 +158,14 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int s = 0; s < kAhead; ++s) issue(s);
     for (int s = 0; s < nst; ++s) {
-        // this wave's loads of stage s have landed (stages s+1, s+2 may not)
+        // this wave's loads of stage s have landed
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * kLoads) : "memory");
         __syncthreads();  // everyone's loads of s landed; everyone is done with s-1
         issue(s + kAhead);  // into the slot of s-1
         const uint8_t* st = smem + (s & (kStages - 1)) * kStageBytes;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks == 2 && s == half_last) break;
             bf16x8 av[2], bv[4];
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb) av[fb] = *(const bf16x8*)(st + a_off[fb][ks]);
