@@ -6,8 +6,9 @@
 // ("How Differential Attention Cancels Common-Mode Noise"), fused into one
 // memory pass ("Throughput and Hardware Realities").  This is the variant for
 // the widest heads: the two O^T accumulators alone fill the 256 accumulation
-// registers (AGPRs), so the score tiles are accumulated in AGPRs as well and
-// the loop differs from the narrow-head kernel in prefill_bf16.hip.
+// registers (AGPRs), the score tiles accumulate in VGPRs (inline-asm
+// products, see mfma_v0), and the loop differs from the narrow-head kernel
+// in prefill_core.h.
 //
 // Work decomposition
 //   One workgroup = 4 wavefronts = 128 query rows of one (batch, head); each
@@ -27,7 +28,7 @@
 //   O_k^T = alpha_k O_k^T + V^T P_k^T   for k = 1, 2,
 // with the operand layouts, the swap23 key permutation that turns score
 // accumulators directly into P^T B operands, the transposing V reads and the
-// lazy running maximum all as described in prefill_bf16.hip.  The O rescale
+// lazy running maximum all as described in prefill_core.h.  The O rescale
 // multiplies the accumulators where they live, in AGPRs.
 //
 // LDS per stage: K1 and K2 row-major [32][d + 8], V row-major [32][dv + 32].
@@ -88,6 +89,29 @@ __device__ __forceinline__ float max16(const f32x16& s) {
     float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
     float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
     return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, s[15]));
+}
+
+// Score products with their accumulators in VGPRs (where the softmax reads
+// them), while the compiler keeps the O accumulators of the P.V builtins in
+// AGPRs.  As builtins they would accumulate in AGPRs too, and with O1 and O2
+// filling all 256 of them the compiler moved an O block out and back every
+// tile (~160 extra instructions per tile).  mfma_v0 starts a chain from zero
+// (two wait states first, for a VALU write of its destination just before),
+// mfma_v continues one.  The compiler does not see an asm product's latency:
+// VALU accesses to the scores come after wait_s (below).
+__device__ __forceinline__ f32x16 mfma_v0(bf16x8 a, bf16x8 b) {
+    f32x16 d;
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// 24 wait states (more than a 32x32x16 product needs) before a VALU access
+// to asm products' results, in an asm that takes the results as operands: no
+// product can be scheduled after it, no access before it
+__device__ __forceinline__ void wait_s(f32x16& s1, f32x16& s2) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s1), "+v"(s2));
 }
 
 // Multiplies every accumulator of o by alpha in place.  The accumulators live
@@ -247,14 +271,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_wide_kernel(PrefillArgs
     auto scores = [&](int buf, f32x16& s1, f32x16& s2) {
         const uint16_t* k1s = smem + buf * C::kStage;
         const uint16_t* k2s = k1s + C::kKElems;
-        s1 = f32x16{};
-        s2 = f32x16{};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             const bf16x8 ka1 = *(const bf16x8*)(k1s + krow * C::kKStride + 16 * kb + 8 * lh);
             const bf16x8 ka2 = *(const bf16x8*)(k2s + krow * C::kKStride + 16 * kb + 8 * lh);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf1[kb], s1, 0, 0, 0);
-            s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka2, qf2[kb], s2, 0, 0, 0);
+            if (kb == 0) {
+                s1 = mfma_v0(ka1, qf1[kb]);
+                s2 = mfma_v0(ka2, qf2[kb]);
+            } else {
+                mfma_v(s1, ka1, qf1[kb]);
+                mfma_v(s2, ka2, qf2[kb]);
+            }
         }
     };
 
@@ -306,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_wide_kernel(PrefillArgs
     // n1, n2: score accumulators of the next tile; s1, s2: tile j's scores
     f32x16 n1, n2, s1, s2;
     scores(0, s1, s2);
+    wait_s(s1, s2);
     mask(0, s1, s2);
 
     int bj = 0;  // stage of tile j; tile j+1 is in (bj+1)%3, tile j+2 goes to (bj+2)%3
@@ -337,6 +365,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_wide_kernel(PrefillArgs
 
         store_tile(bw);      // tile j+2 (stale and unused once past the end)
         load_tile(j + 3);    // clamped rows once past the end
+        wait_s(n1, n2);  // before the masking and the copies read them
         mask(j + 1, n1, n2);
         __syncthreads();
         s1 = n1;
