@@ -45,16 +45,20 @@ PMC_BENCH_ARGS = ["--steps", "3", "--warmup", "1", "--no-cpu", "--no-backward", 
 COPY_BYTES = 1 << 30
 COPY_GRID = COPY_BYTES // 16  # threads of the vectorised copy (4 floats per thread)
 
-# kernel -> (workload it runs on in bench.py, source file, algorithmic bytes per launch)
+# kernel -> (workload it runs on in bench.py, its source files joined by "+")
 KERNELS = {
-    "prefill_bf16_kernel": ("causal_prefill_bf16", "prefill_bf16.hip"),
+    "prefill_bf16_kernel": ("causal_prefill_bf16", "prefill_core.h+prefill_bf16.hip"),
     "decode_partial_kernel": ("decode_bf16", "decode.hip"),
 }
 
 
-def source_sha(fname: str) -> str:
-    with open(os.path.join(CSRC, fname), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(fnames: str) -> str:
+    """sha256 of the named source files, concatenated in order."""
+    h = hashlib.sha256()
+    for fname in fnames.split("+"):
+        with open(os.path.join(CSRC, fname), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _commands(out: str):
@@ -298,7 +302,7 @@ def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
             vals.get("SQ_INSTS_VALU_TRANS_F32", 0) / vals["SQ_INSTS_MFMA"])
         derived["LDS instructions per MFMA"] = vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"]
     src = {"prefill_bf16_wide_kernel": "prefill_bf16_wide.hip"}.get(
-        kernel, KERNELS.get(kernel, (None, "prefill_bf16.hip"))[1])
+        kernel, KERNELS.get(kernel, (None, "prefill_core.h+prefill_bf16.hip"))[1])
     lines = [f"# {kernel} on {workload}: SQ counters per dispatch", "",
              "Commands (from /tmp, TMPDIR=/tmp; written by "
              f"`python3 profile_kernels.py counters --workload {workload}`):", ""]
