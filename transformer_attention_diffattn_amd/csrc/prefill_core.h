@@ -706,28 +706,40 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     __syncthreads();
     const int other = map ^ 1;
     const float cs = map ? lam_h / L : 1.f / L;
+    // exchange layout per (query block, receiving map): [db][g][lane] float4
+    // holding registers 4g .. 4g+3 of block db, so each lane moves 16 bytes
+    // per instruction and 16 lanes cover 256 contiguous bytes
     float* xchg = (float*)smem;
     {
-        float* dst = xchg + (qb * 2 + other) * (NH * 16 * 64) + lane;
+        float* dst = xchg + (qb * 2 + other) * (NH * 16 * 64) + 4 * lane;
 #pragma unroll
         for (int db = 0; db < NH; ++db) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dst[(db * 16 + r) * 64] = product(map ? o[db][r] : o[NH + db][r], cs);
+            for (int g = 0; g < 4; ++g) {
+                const f32x16& src = map ? o[db] : o[NH + db];
+                *(float4*)(dst + (db * 4 + g) * 256) =
+                    make_float4(product(src[4 * g], cs), product(src[4 * g + 1], cs),
+                                product(src[4 * g + 2], cs), product(src[4 * g + 3], cs));
+            }
         }
     }
     __syncthreads();
     float x[NH][16];
     {
-        const float* src = xchg + (qb * 2 + map) * (NH * 16 * 64) + lane;
+        const float* src = xchg + (qb * 2 + map) * (NH * 16 * 64) + 4 * lane;
 #pragma unroll
         for (int db = 0; db < NH; ++db) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float got = src[(db * 16 + r) * 64];
-                const float own = map ? o[NH + db][r] : o[db][r];
-                x[db][r] = map ? diff_of_products(got, 1.f, own, cs)
-                               : diff_of_products(own, cs, got, 1.f);
+            for (int g = 0; g < 4; ++g) {
+                const float4 got4 = *(const float4*)(src + (db * 4 + g) * 256);
+                const float got[4] = {got4.x, got4.y, got4.z, got4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    const float own = map ? o[NH + db][r] : o[db][r];
+                    x[db][r] = map ? diff_of_products(got[e], 1.f, own, cs)
+                                   : diff_of_products(own, cs, got[e], 1.f);
+                }
             }
         }
     }
