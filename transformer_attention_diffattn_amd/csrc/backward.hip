@@ -288,14 +288,16 @@ void bwd_dkdv_kernel(BackwardArgs a) {
     const float* del2 = a.delta + ((size_t)BH + bh) * a.Nq;
     // row terms: thread t < 128 carries term t / 32 of query t % 32
     const int which = threadIdx.x >> 5;
+    const float row_scale = which < 2 ? kLog2e : 1.f;  // log-sum-exps to log2 units
     auto put_row = [&](int b, float v) {
-        if (threadIdx.x < 128) ((float*)&srow[b][threadIdx.x & 31])[which] = v;
+        if (threadIdx.x < 128) ((float*)&srow[b][threadIdx.x & 31])[which] = v * row_scale;
     };
     const float* rsrc = which == 0 ? lse1 : which == 1 ? lse2 : which == 2 ? del1 : del2;
+    // rows past Nq load the last row's terms (an index clamp, not a select
+    // on the loaded value, so nothing waits for the load before put_row);
+    // their pairs are masked
     auto load_row = [&](int qt) {
-        const int q = qt * 32 + (threadIdx.x & 31);
-        const float v = (threadIdx.x < 128 && q < a.Nq) ? rsrc[q] : 0.f;
-        return which < 2 ? v * kLog2e : v;
+        return rsrc[min(qt * 32 + (int)(threadIdx.x & 31), a.Nq - 1)];
     };
     RowTile<D> t1, t2;
     RowTile<DV> td;
@@ -324,23 +326,52 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         const uint16_t* sq2 = sq[buf][1];
         const uint16_t* sd_ = sd[buf];
         const float4* sr = srow[buf];
-        // S_k = Q_k K_k^T and dP = dD V^T, query rows in swap23 order
+        // S_k = Q_k K_k^T and dP = dD V^T, query rows in swap23 order.  All
+        // operand reads are issued before the first product (one wave per
+        // SIMD: nothing else hides the LDS latency of a read issued right
+        // before its product)
         const int qr = swap23(l32);
+        bf16x8 aq1[NKB], aq2[NKB], ad[NVB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            aq1[kb] = rd_row(sq1, KS, qr, 16 * kb, lh);
+            aq2[kb] = rd_row(sq2, KS, qr, 16 * kb, lh);
+        }
+#pragma unroll
+        for (int c = 0; c < NVB; ++c) ad[c] = rd_row(sd_, VS, qr, 16 * c, lh);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            s1 = mfma(rd_row(sq1, KS, qr, 16 * kb, lh), k1f[kb], s1);
-            s2 = mfma(rd_row(sq2, KS, qr, 16 * kb, lh), k2f[kb], s2);
+            s1 = mfma(aq1[kb], k1f[kb], s1);
+            s2 = mfma(aq2[kb], k2f[kb], s2);
         }
 #pragma unroll
-        for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sd_, VS, qr, 16 * c, lh), vf[c], dp);
+        for (int c = 0; c < NVB; ++c) dp = mfma(ad[c], vf[c], dp);
+        // the transposed operands of the dV and dK products (independent of
+        // the vector work below) and the row terms, in flight meanwhile
+        bf16x8 ov[2][NDB], o1c[2][NCB], o2c[2][NCB];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int cb = 0; cb < NDB; ++cb) ov[kk][cb] = rd_col(sd_, VS, 16 * kk, 32 * cb, lane);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                o1c[kk][cb] = rd_col(sq1, KS, 16 * kk, 32 * cb, lane);
+                o2c[kk][cb] = rd_col(sq2, KS, 16 * kk, 32 * cb, lane);
+            }
+        }
+        float4 trow[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) trow[r] = sr[16 * (r >> 3) + 8 * lh + (r & 7)];
+        __builtin_amdgcn_sched_barrier(0);
         float wd[16], d1[16], d2[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
             const int q = qt * 32 + qi;
             const bool ok = kok && q < a.Nq && (!CAUSAL || key <= q);
-            const float4 t = sr[qi];
+            const float4 t = trow[r];
             // masked pairs take exp2(-inf) = 0; the arguments are formed for
             // every lane (the empty asm keeps the compiler from moving them,
             // and the row-term read, into a branch per element)
@@ -360,12 +391,11 @@ void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int cb = 0; cb < NDB; ++cb)
-                dvt[cb] = mfma(rd_col(sd_, VS, 16 * kk, 32 * cb, lane), pwd[kk], dvt[cb]);
+            for (int cb = 0; cb < NDB; ++cb) dvt[cb] = mfma(ov[kk][cb], pwd[kk], dvt[cb]);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                dk1t[cb] = mfma(rd_col(sq1, KS, 16 * kk, 32 * cb, lane), pd1[kk], dk1t[cb]);
-                dk2t[cb] = mfma(rd_col(sq2, KS, 16 * kk, 32 * cb, lane), pd2[kk], dk2t[cb]);
+                dk1t[cb] = mfma(o1c[kk][cb], pd1[kk], dk1t[cb]);
+                dk2t[cb] = mfma(o2c[kk][cb], pd2[kk], dk2t[cb]);
             }
         }
         // the other buffer was last read before the previous barrier

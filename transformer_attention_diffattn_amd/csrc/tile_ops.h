@@ -52,10 +52,18 @@ __device__ __forceinline__ void pack(const float (&x)[16], bf16x8 (&o)[2]) {
         for (int j = 0; j < 8; ++j) o[c][j] = (__bf16)x[8 * c + j];
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (clamped to [0, 2^31 - 1]);
+// loads at offsets past the end return zeros and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
 // A tile of 32 rows of a [n][W] bf16 tensor, moved in two steps so that the
 // global loads of the next tile are in flight while the current one is used:
-// load() into registers (rows at or past n read as zero), store() into a
-// padded LDS tile.
+// load() into registers (rows at or past n read as zero, by the buffer
+// bounds: no select on the loaded value, so nothing waits for the load before
+// store()), store() into a padded LDS tile.
 template <int W>
 struct RowTile {
     static constexpr int kCpr = W / 8;  // 16-byte chunks per row
@@ -63,13 +71,14 @@ struct RowTile {
     static constexpr int kPer = (kChunks + kBwdThreads - 1) / kBwdThreads;
     uint4 r[kPer];
     __device__ __forceinline__ void load(const uint16_t* g, int64_t row0, int64_t n) {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g + row0 * W, (n - row0) * W * 2);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int c = threadIdx.x + kBwdThreads * i;
             const int row = c / kCpr, ch = c % kCpr;
-            r[i] = (c < kChunks && row0 + row < n)
-                       ? *(const uint4*)(g + (row0 + row) * W + 8 * ch)
-                       : make_uint4(0, 0, 0, 0);
+            // (chunks past the tile, c >= kChunks, are loaded and not stored)
+            r[i] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (row * W + 8 * ch) * 2, 0, 0));
         }
     }
     __device__ __forceinline__ void store(uint16_t* t) const {
