@@ -271,16 +271,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_wide_kernel(PrefillArgs
     auto scores = [&](int buf, f32x16& s1, f32x16& s2) {
         const uint16_t* k1s = smem + buf * C::kStage;
         const uint16_t* k2s = k1s + C::kKElems;
+        // all K operand reads first: with one wave per SIMD nothing else would
+        // hide the LDS latency of a read issued right before its product
+        bf16x8 ka1[NKB], ka2[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            const bf16x8 ka1 = *(const bf16x8*)(k1s + krow * C::kKStride + 16 * kb + 8 * lh);
-            const bf16x8 ka2 = *(const bf16x8*)(k2s + krow * C::kKStride + 16 * kb + 8 * lh);
+            ka1[kb] = *(const bf16x8*)(k1s + krow * C::kKStride + 16 * kb + 8 * lh);
+            ka2[kb] = *(const bf16x8*)(k2s + krow * C::kKStride + 16 * kb + 8 * lh);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
             if (kb == 0) {
-                s1 = mfma_v0(ka1, qf1[kb]);
-                s2 = mfma_v0(ka2, qf2[kb]);
+                s1 = mfma_v0(ka1[kb], qf1[kb]);
+                s2 = mfma_v0(ka2[kb], qf2[kb]);
             } else {
-                mfma_v(s1, ka1, qf1[kb]);
-                mfma_v(s2, ka2, qf2[kb]);
+                mfma_v(s1, ka1[kb], qf1[kb]);
+                mfma_v(s2, ka2[kb], qf2[kb]);
             }
         }
     };
@@ -352,14 +359,28 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_wide_kernel(PrefillArgs
         bf16x8 p1[2], p2[2];
         probabilities(s1, sl2, base1, l1, p1);
         probabilities(s2, sl2, base2, l2, p2);
-        // step 2: P.V for both maps, each V operand read once
+        // step 2: P.V for both maps, each V operand read once; the reads in
+        // groups of four operands, each group issued before the previous
+        // group's products
+        constexpr int kGrp = 4;
+        bf16x8 vcur[kGrp], vnxt[kGrp];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int u = 0; u < kGrp; ++u) vnxt[u] = v_operand(bj, u >> 1, u & 1);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 va = v_operand(bj, db, kb);
-                o1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p1[kb], o1[db], 0, 0, 0);
-                o2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p2[kb], o2[db], 0, 0, 0);
+        for (int g0 = 0; g0 < 2 * NDB; g0 += kGrp) {
+#pragma unroll
+            for (int u = 0; u < kGrp; ++u) vcur[u] = vnxt[u];
+            if (g0 + kGrp < 2 * NDB) {
+#pragma unroll
+                for (int u = 0; u < kGrp; ++u)
+                    vnxt[u] = v_operand(bj, (g0 + kGrp + u) >> 1, (g0 + kGrp + u) & 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kGrp; ++u) {
+                const int db = (g0 + u) >> 1, kb = (g0 + u) & 1;
+                o1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[u], p1[kb], o1[db], 0, 0, 0);
+                o2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[u], p2[kb], o2[db], 0, 0, 0);
             }
         }
 
