@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """rocprofv3 passes behind the benchmark's roofline figures.
 
-    python3 profile_kernels.py run [--out gpurun_out/prof]
-    python3 profile_kernels.py summarize [--out gpurun_out/prof]
-    python3 profile_kernels.py counters [--workload NAME] [--out gpurun_out/prof]
+    python3 profile_kernels.py run [--out DIR]
+    python3 profile_kernels.py summarize [--out DIR]
+    python3 profile_kernels.py counters [--workload NAME] [--out DIR]
+
+(DIR: where rocprofv3 writes its raw output, default prof_out/.)
 
 `run` starts three rocprofv3 child processes over bench.py (each with its own
 time limit, from /tmp with TMPDIR=/tmp):
@@ -151,7 +153,7 @@ def summarize(out: str) -> None:
     copy_kib = COPY_BYTES / 1024
     f_cal, w_cal = _calibration(fetch), _calibration(write)
     f_factor, w_factor = copy_kib / f_cal, copy_kib / w_cal
-    cmds = _commands("gpurun_out/prof")
+    cmds = _commands(os.path.relpath(out, ROOT))
     os.makedirs(PROFILES, exist_ok=True)
     sys.path.insert(0, ROOT)
     import workloads
@@ -309,7 +311,7 @@ def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
     py = sys.executable or "python3"
     for i in range(len(COUNTER_PASSES)):
         shown = ["python3" if c == py else (os.path.relpath(c, ROOT) if c.startswith(ROOT) else c)
-                 for c in _counter_cmd("gpurun_out/prof", i, workload)]
+                 for c in _counter_cmd(os.path.relpath(out, ROOT), i, workload)]
         lines.append(f"- `{' '.join(shown)}`")
     lines += ["", "Kernel cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); "
               "SIMD cycles = kernel cycles x 1024 SIMDs (256 CUs x 4).", "",
@@ -345,7 +347,7 @@ def load(kernel: str):
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("action", choices=["run", "summarize", "counters", "counters-summarize"])
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "prof_out"))
     ap.add_argument("--workload", default="causal_prefill_bf16")
     ap.add_argument("--profiles-dir", default=PROFILES,
                     help="where summaries go (on a remote GPU box: a folder that is copied back)")
