@@ -25,7 +25,10 @@
 //   leaves the SIMD to the other.  Waves w and w + 4 run on the same SIMD, one
 //   per map.  K1, K2 and V stream through an 8-stage LDS ring in tiles of 32
 //   keys, loaded 6 tiles ahead of use; each wave reads the K tile of its own
-//   map and the shared V tile.
+//   map and the shared V tile.  The main loop is unrolled over one turn of
+//   the ring, so every stage address is an instruction's immediate offset
+//   (K and V sit in two rings of that depth, each under the 64 KB reach of
+//   the offset) and the loop spends no instructions on stage arithmetic.
 //
 //   Iteration j of a wave issues, in one branch-free block,
 //     MFMA  scores of tile j+1, P.V of tile j-1;
@@ -124,6 +127,12 @@ struct Cfg {
     static constexpr int kKElems = kBc * kKRow / 2;        // K tile, in 16-bit units
     static constexpr int kVElems = kBc * DV;
     static constexpr int kStage = 2 * kKElems + kVElems;  // 16-bit units per stage
+    // the ring is two rings: K1 and K2 of stage s at s kKStage, V of stage s at
+    // kVRing + s kVStage, so that any stage's operands sit less than 64 KB
+    // past a per-lane base (the LDS instructions' immediate offset)
+    static constexpr int kKStage = 2 * kKElems;
+    static constexpr int kVStage = kVElems;
+    static constexpr int kVRing = kStages * kKStage;
     static constexpr int kKChunks = kBc * kKRow / 16;      // 16-byte chunks per K tile
     static constexpr int kVChunks = kBc * DV / 8;
     static constexpr int kChunks = 2 * kKChunks + kVChunks;
@@ -337,10 +346,9 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     for (int i = 0; i < C::kLoads; ++i) {
         if constexpr (F8) {
             if (i == 0) {  // V: chunk group wave_u
-                const int c0 = 2 * C::kKChunks + 64 * wave_u;
                 const int pos = 64 * wave_u + lane;
                 const int row = pos / (DV / 8);
-                m0_off[i] = 16u * (uint32_t)c0;
+                m0_off[i] = 2u * C::kVRing + 16u * 64u * (uint32_t)wave_u;
                 src[i] = 2;
                 ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz<DV>(row));
             } else {  // K1 (i = 1) or K2 (i = 2): 256 bytes, rows 4 wave_u ..
@@ -362,6 +370,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
             } else {
                 const int pos = c0 - 2 * C::kKChunks + lane;
                 const int row = pos / (DV / 8);
+                m0_off[i] = 2u * C::kVRing + 16u * (uint32_t)(c0 - 2 * C::kKChunks);
                 src[i] = 2;
                 ld_off[i] = row * DV * 2 + 16 * ((pos % (DV / 8)) ^ v_swz<DV>(row));
             }
@@ -384,11 +393,14 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
         tile_bytes[i] = kBc * row_bytes;
         region_bytes[i] = FLAT ? (uint32_t)bytes : 0u;
     }
-    auto issue_tile = [&](int kt) {
-        const uint32_t stage = smem_base + 2u * (uint32_t)(stage_of(kt) * C::kStage);
+    static_assert(F8 || C::kKStage == C::kVStage, "bf16 loads share one stage stride");
+    // tile kt into ring stage st (= kt mod kStages)
+    auto issue_tile = [&](int kt, int st) {
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
-            const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + m0_off[i]);
+            const uint32_t stride = 2u * (uint32_t)((F8 && i == 0) ? C::kVStage : C::kKStage);
+            const uint32_t m0 =
+                __builtin_amdgcn_readfirstlane(smem_base + m0_off[i] + (uint32_t)st * stride);
             const bool dw = F8 && i > 0;  // 4-byte load
             // Tiles past this workgroup's last one read out of range: the
             // instruction count per tile stays fixed (the waits count on it)
@@ -444,7 +456,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
         k_off[kb] = map * C::kKElems + krow * (C::kKRow / 2) +
                     8 * ((F8 ? 2 * lh + kb : 2 * kb + lh) ^ k_swz_rb<C::kKRow>(krow));
     auto k_operand = [&](int buf, int kb) {
-        return *(const bf16x8*)(smem + buf * C::kStage + k_off[kb]);
+        return *(const bf16x8*)(smem + buf * C::kKStage + k_off[kb]);
     };
     // one score product: bf16 k = 16 step kb, or the whole e4m3 row (k = 64)
     auto score_mfma = [&](int buf, int kb, f32x16 c) {
@@ -481,13 +493,13 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     // i.e. chunk 4 db + 2 (vg%2) + (lane%4)/2 and byte 8 (lane%2) in it
     const int vg = lane >> 4;
     const int ve = (lane & 15) >> 2;
-    const int v_lane_row = 2 * C::kKElems + (8 * (vg >> 1) + ve) * DV + 4 * (lane & 1);  // 16-bit units
+    const int v_lane_row = C::kVRing + (8 * (vg >> 1) + ve) * DV + 4 * (lane & 1);  // 16-bit units
     int v_off[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
         v_off[db] = v_lane_row + 8 * ((4 * db + 2 * (vg & 1) + ((lane & 3) >> 1)) ^ v_swz<DV>(ve));
     auto v_operand = [&](int buf, int db, int kb) {
-        const uint16_t* vp = smem + buf * C::kStage + v_off[db] + 16 * kb * DV;
+        const uint16_t* vp = smem + buf * C::kVStage + v_off[db] + 16 * kb * DV;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)vp);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -530,8 +542,8 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     // its own loads, which would also drain every tile load issued before that
     // use; so the Q fragments are taken (and waited for) right after tiles 0
     // and 1, which the first iteration needs anyway, and the rest follow.
-    issue_tile(0);
-    issue_tile(1);
+    issue_tile(0, 0);
+    issue_tile(1, 1);
     if constexpr (F8) {
         asm volatile("" ::"v"(qf8));
     } else {
@@ -539,7 +551,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
         for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(qf[kb]));
     }
 #pragma unroll
-    for (int t0 = 2; t0 < C::kAhead; ++t0) issue_tile(t0);
+    for (int t0 = 2; t0 < C::kAhead; ++t0) issue_tile(t0, t0);
     wait_tiles(std::integral_constant<int, C::kAhead - 2>{});
     __syncthreads();
     scores(0, A.s);
@@ -571,17 +583,21 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
 
     // One iteration j (see the header); cur holds tile j, oth tile j-1 and
     // then j+1.  PREV: tile j-1 exists; NEXT: tile j+1 exists.
-    auto iteration = [&](auto prev, auto next, int j, TileState& cur, TileState& oth) {
+    // R: j mod kStages when known at compile time (stage offsets then fold into
+    // the LDS instructions), else -1
+    auto iteration = [&](auto res, auto prev, auto next, int j, TileState& cur, TileState& oth) {
+        constexpr int R = decltype(res)::value;
         constexpr bool PREV = decltype(prev)::value;
         constexpr bool NEXT = decltype(next)::value;
+        auto st = [&](int d) { return R >= 0 ? ((R + d) & (C::kStages - 1)) : stage_of(j + d); };
         const float base = m == -INFINITY ? 0.f : m;
 
         bf16x8 ka[F8 ? 2 : NKB], va[kPairsV];
         if constexpr (NEXT) {
 #pragma unroll
-            for (int kb = 0; kb < (F8 ? 2 : NKB); ++kb) ka[kb] = k_operand(stage_of(j + 1), kb);
+            for (int kb = 0; kb < (F8 ? 2 : NKB); ++kb) ka[kb] = k_operand(st(1), kb);
         }
-        const int vbuf = stage_of(j - 1);
+        const int vbuf = st(-1);
         if constexpr (PREV) {
 #pragma unroll
             for (int q = 0; q < kLookahead; ++q) va[q] = v_operand(vbuf, q >> 1, q & 1);
@@ -633,7 +649,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
                 if (pair_slot(k) + 2 == slot)
                     pack_pair(cur.p, 2 * k, xs[2 * k], xs[2 * k + 1], (k & 1) ? tb : ta);
             }
-            if (slot == kLoadSlot) issue_tile(j + C::kAhead);  // zeros once past the end
+            if (slot == kLoadSlot) issue_tile(j + C::kAhead, st(C::kAhead));  // zeros once past the end
         }
         // Keep the common-path probabilities ahead of the rare branch below
         // (which forms them again) rather than sunk into its other side.
@@ -670,23 +686,37 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
 
     const bool_c<true> T;
     const bool_c<false> F;
+    const std::integral_constant<int, -1> Rd;  // stage from j at run time
+    auto Rs = [](auto r) { return std::integral_constant<int, decltype(r)::value>{}; };
     if (nkt == 1) {
-        iteration(F, F, 0, A, B);
+        iteration(Rd, F, F, 0, A, B);
         pv(stage_of(0), A.p);
     } else {
-        iteration(F, T, 0, A, B);
-        // tile j lives in A for even j and in B for odd j
+        iteration(std::integral_constant<int, 0>{}, F, T, 0, A, B);
+        // tile j lives in A for even j and in B for odd j; j = 1 mod kStages in
+        // the unrolled loop, whose iterations are all followed by another
         int j = 1;
+        static_assert(C::kStages == 8, "the unrolled loop covers one turn of the ring");
+        for (; j + 7 < nkt - 1; j += 8) {
+            iteration(Rs(std::integral_constant<int, 1>{}), T, T, j, B, A);
+            iteration(Rs(std::integral_constant<int, 2>{}), T, T, j + 1, A, B);
+            iteration(Rs(std::integral_constant<int, 3>{}), T, T, j + 2, B, A);
+            iteration(Rs(std::integral_constant<int, 4>{}), T, T, j + 3, A, B);
+            iteration(Rs(std::integral_constant<int, 5>{}), T, T, j + 4, B, A);
+            iteration(Rs(std::integral_constant<int, 6>{}), T, T, j + 5, A, B);
+            iteration(Rs(std::integral_constant<int, 7>{}), T, T, j + 6, B, A);
+            iteration(Rs(std::integral_constant<int, 0>{}), T, T, j + 7, A, B);
+        }
         for (; j + 1 < nkt - 1; j += 2) {
-            iteration(T, T, j, B, A);
-            iteration(T, T, j + 1, A, B);
+            iteration(Rd, T, T, j, B, A);
+            iteration(Rd, T, T, j + 1, A, B);
         }
         if (j < nkt - 1) {
-            iteration(T, T, j, B, A);
-            iteration(T, F, j + 1, A, B);
+            iteration(Rd, T, T, j, B, A);
+            iteration(Rd, T, F, j + 1, A, B);
             pv(stage_of(j + 1), A.p);
         } else {
-            iteration(T, F, j, B, A);
+            iteration(Rd, T, F, j, B, A);
             pv(stage_of(j), B.p);
         }
     }
