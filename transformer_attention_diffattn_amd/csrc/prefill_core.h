@@ -228,6 +228,16 @@ __device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, int64_t bytes) {
 // The bf16 probabilities p[e], p[e+1] of a tile packed into pb, added to a
 // row partial sum with one dot product against (1, 1): the sum is taken over
 // the same rounded values that enter P.V.
+// The first pair of a sum: the bf16 dot product with a zero accumulator as
+// one instruction (the compiler would zero a register and accumulate).
+__device__ __forceinline__ void pack_pair_first(bf16x8 (&pb)[2], int e, float pa, float pc, float& sum) {
+    const bf16x2 pr = {(__bf16)pa, (__bf16)pc};
+    u32x4 w = __builtin_bit_cast(u32x4, pb[e >> 3]);
+    w[(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+    pb[e >> 3] = __builtin_bit_cast(bf16x8, w);
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(sum) : "v"(__builtin_bit_cast(uint32_t, pr)), "s"(0x3f803f80u));
+}
+
 __device__ __forceinline__ void pack_pair(bf16x8 (&pb)[2], int e, float pa, float pc, float& sum) {
     const bf16x2 pr = {(__bf16)pa, (__bf16)pc};
     u32x4 w = __builtin_bit_cast(u32x4, pb[e >> 3]);
@@ -321,7 +331,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     const int nkt_all = (a.Nk + kBc - 1) / kBc;
     const int nkt = CAUSAL ? min(nkt_all, (qt * C::kBr + C::kBr + kBc - 1) / kBc) : nkt_all;
     // leading tiles in which no row of this wave masks a key
-    const int nfull = CAUSAL ? min(a.Nk / kBc, (wq0 + 1) / kBc) : a.Nk / kBc;
+    const int nfull = __builtin_amdgcn_readfirstlane(CAUSAL ? min(a.Nk / kBc, (wq0 + 1) / kBc) : a.Nk / kBc);
 
     // Tile loads go from global memory straight into the LDS ring
     // (buffer_load_dwordx4 ... lds: lane i of an instruction writes its 16
@@ -602,7 +612,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
 #pragma unroll
             for (int q = 0; q < kLookahead; ++q) va[q] = v_operand(vbuf, q >> 1, q & 1);
         }
-        float ta = 0.f, tb = 0.f;
+        float ta, tb;  // set by the first pair of each
         float xs[16];  // probabilities in flight, by accumulator register
 
 #pragma unroll
@@ -646,8 +656,12 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
                     xs[2 * k] = __builtin_amdgcn_exp2f(xs[2 * k]);
                     xs[2 * k + 1] = __builtin_amdgcn_exp2f(xs[2 * k + 1]);
                 }
-                if (pair_slot(k) + 2 == slot)
-                    pack_pair(cur.p, 2 * k, xs[2 * k], xs[2 * k + 1], (k & 1) ? tb : ta);
+                if (pair_slot(k) + 2 == slot) {
+                    if (k < 2)
+                        pack_pair_first(cur.p, 2 * k, xs[2 * k], xs[2 * k + 1], (k & 1) ? tb : ta);
+                    else
+                        pack_pair(cur.p, 2 * k, xs[2 * k], xs[2 * k + 1], (k & 1) ? tb : ta);
+                }
             }
             if (slot == kLoadSlot) issue_tile(j + C::kAhead, st(C::kAhead));  // zeros once past the end
         }
