@@ -38,7 +38,7 @@
 //   the ragged last tile only) and the lazy-maximum test of tile j (below),
 //   whose body almost never runs.  None of the three streams waits for
 //   another inside the block, so the two waves of a SIMD can overlap one's
-//   matrix work with the other's vector work.  One barrier per tile.
+//   matrix work with the other's vector work.  One barrier per two tiles.
 //
 // Per tile and wave, on MFMA v_mfma_f32_32x32x16_bf16 (k = the wave's map):
 //   S_k^T = K_k Q_k^T          (keys on the M axis, the wave's 32 queries on N),
@@ -122,7 +122,7 @@ template <int D, int DV, bool F8 = false>
 struct Cfg {
     static constexpr int kBr = kBlocks * 32;
     static constexpr int kStages = 8;                      // LDS ring (a power of two)
-    static constexpr int kAhead = 6;                       // tiles loaded ahead of use
+    static constexpr int kAhead = 5;                       // tiles loaded ahead of use
     static constexpr int kKRow = F8 ? D : 2 * D;           // bytes per K row
     static constexpr int kKElems = kBc * kKRow / 2;        // K tile, in 16-bit units
     static constexpr int kVElems = kBc * DV;
@@ -144,9 +144,10 @@ struct Cfg {
     static_assert(F8 || kKChunks % 64 == 0, "K regions must start on an instruction boundary");
     static_assert(!F8 || (kVChunks == 64 * kWaves && kKChunks * 16 == 256 * kWaves),
                   "e4m3 tile: one V load and one K1 and one K2 load per wave");
-    // a stage is refilled kStages - kAhead tiles after the barrier that ends
-    // its last reads (V of tile t is read in iteration t + 1)
-    static_assert(kAhead + 2 <= kStages, "ring too small for the load distance");
+    // a stage is refilled kAhead tiles after its tile, by iteration t + 8 -
+    // kAhead for tile t, whose V is last read in iteration t + 1; with a
+    // barrier after every odd iteration one always lies between the two
+    static_assert(kAhead + 3 <= kStages, "ring too small for the load distance");
     // epilogue, reusing the ring: the two half-row exchanges (one float per
     // query block, accumulator and lane), the GroupNorm statistics (two
     // floats per wave and lane) and the bf16 output staging (32 rows by DV/2
@@ -547,7 +548,8 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     };
     TileState A, B;
 
-    // prologue: tiles 0 .. kAhead-1 in flight; tiles 0 and 1 complete.  The
+    // prologue: tiles 0 .. kAhead-1 in flight; tiles 0, 1 and 2 complete (the
+    // first barrier in the loop comes after iteration 1).  The
     // compiler waits for the Q loads before their first use by counting only
     // its own loads, which would also drain every tile load issued before that
     // use; so the Q fragments are taken (and waited for) right after tiles 0
@@ -562,7 +564,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     }
 #pragma unroll
     for (int t0 = 2; t0 < C::kAhead; ++t0) issue_tile(t0, t0);
-    wait_tiles(std::integral_constant<int, C::kAhead - 2>{});
+    wait_tiles(std::integral_constant<int, C::kAhead - 3>{});
     __syncthreads();
     scores(0, A.s);
     if (nfull < 1) mask(0, A.s);
@@ -692,10 +694,13 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
             for (int e = 0; e < 16; e += 2) prob_pair(cur.s, e, sl2, nb, cur.p, tsum);
         }
         l += tsum;
-        // tile j+2 (read from the next iteration on) must have landed; tiles
-        // j+3 .. j+kAhead may still be in flight
-        wait_tiles(std::integral_constant<int, C::kAhead - 2>{});
-        __syncthreads();
+        // a barrier after odd iterations only: tiles j+2 and j+3 (read by the
+        // next two) must have landed; tiles j+4 .. j+kAhead may still be in flight
+        const bool odd = R >= 0 ? (R & 1) : (j & 1);
+        if (odd) {
+            wait_tiles(std::integral_constant<int, C::kAhead - 3>{});
+            __syncthreads();
+        }
     };
 
     const bool_c<true> T;
