@@ -759,23 +759,32 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     // holding registers 4g .. 4g+3 of block db, so each lane moves 16 bytes
     // per instruction and 16 lanes cover 256 contiguous bytes
     float* xchg = (float*)smem;
-    {
+    // the map is wave-uniform: branch on it (a select would form both sides
+    // of every element)
+    const bool lambda_map = __builtin_amdgcn_readfirstlane(map) != 0;
+    auto send = [&](auto h0) {  // blocks [H0, H0 + NH) go to the other wave
+        constexpr int H0 = decltype(h0)::value;
         float* dst = xchg + (qb * 2 + other) * (NH * 16 * 64) + 4 * lane;
 #pragma unroll
         for (int db = 0; db < NH; ++db) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x16& src = map ? o[db] : o[NH + db];
+                const f32x16& src = o[H0 + db];
                 *(float4*)(dst + (db * 4 + g) * 256) =
                     make_float4(product(src[4 * g], cs), product(src[4 * g + 1], cs),
                                 product(src[4 * g + 2], cs), product(src[4 * g + 3], cs));
             }
         }
-    }
+    };
+    if (lambda_map)
+        send(std::integral_constant<int, 0>{});
+    else
+        send(std::integral_constant<int, NH>{});
     __syncthreads();
     float x[NH][16];
-    {
-        const float* src = xchg + (qb * 2 + map) * (NH * 16 * 64) + 4 * lane;
+    auto form = [&](auto lm) {  // D on the wave's own blocks
+        constexpr bool LM = decltype(lm)::value;
+        const float* src = xchg + (qb * 2 + (LM ? 1 : 0)) * (NH * 16 * 64) + 4 * lane;
 #pragma unroll
         for (int db = 0; db < NH; ++db) {
 #pragma unroll
@@ -785,13 +794,16 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g + e;
-                    const float own = map ? o[NH + db][r] : o[db][r];
-                    x[db][r] = map ? diff_of_products(got[e], 1.f, own, cs)
-                                   : diff_of_products(own, cs, got[e], 1.f);
+                    x[db][r] = LM ? diff_of_products(got[e], 1.f, o[NH + db][r], cs)
+                                  : diff_of_products(o[db][r], cs, got[e], 1.f);
                 }
             }
         }
-    }
+    };
+    if (lambda_map)
+        form(bool_c<true>{});
+    else
+        form(bool_c<false>{});
     if constexpr (SAVE) {
         // training forward: D before the normalisation, and each map's
         // log-sum-exp (m and l share the lazy maximum, so m + log2 l is exact)
