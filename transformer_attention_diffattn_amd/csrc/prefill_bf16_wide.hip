@@ -32,10 +32,11 @@
 // multiplies the accumulators where they live, in AGPRs.
 //
 // LDS per stage: K1 and K2 row-major [32][d + 8], V row-major [32][dv + 32].
-// Global loads clamp the key index to the last valid row instead of branching;
-// scores of keys past the end are masked, so the clamped rows contribute 0.
+// Global loads go through buffer descriptors that end at the last key, so rows
+// past the end read as zero without a branch; their scores are masked.
 
 #include "internal.h"
+#include "tile_ops.h"
 
 #include <math.h>
 
@@ -220,28 +221,38 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_wide_kernel(PrefillArgs
 
     const int nkt_all = (a.Nk + kBc - 1) / kBc;
     const int nkt = CAUSAL ? min(nkt_all, (qt * C::kBr + C::kBr + kBc - 1) / kBc) : nkt_all;
-    const int last_key = a.Nk - 1;
 
     u32x4 rk1[C::kKLoads], rk2[C::kKLoads], rv[C::kVLoads];
 
-    // global -> registers; key indices clamp to the last row (masked later)
+    // global -> registers through buffer loads: one descriptor per tensor and
+    // tile (scalar work) starting at the tile's first key, per-lane byte
+    // offsets fixed for the whole item; rows past the last key read as zero
+    // (their scores are masked, so they contribute nothing)
+    uint32_t k_voff[C::kKLoads], v_voff[C::kVLoads];
+#pragma unroll
+    for (int i = 0; i < C::kKLoads; ++i) {
+        const int c = tid + i * kThreads;
+        k_voff[i] = (uint32_t)(((c / (D / 8)) * D + (c % (D / 8)) * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kVLoads; ++i) {
+        const int c = tid + i * kThreads;
+        v_voff[i] = (uint32_t)(((c / (DV / 8)) * DV + (c % (DV / 8)) * 8) * 2);
+    }
     auto load_tile = [&](int kt) {
         const int key0 = kt * kBc;
+        const int64_t left = (int64_t)a.Nk - key0;  // <= 0 past the end: all zeros
+        const __amdgpu_buffer_rsrc_t r1 = tile::buffer_rsrc(gk1 + (size_t)key0 * D, left * D * 2);
+        const __amdgpu_buffer_rsrc_t r2 = tile::buffer_rsrc(gk2 + (size_t)key0 * D, left * D * 2);
+        const __amdgpu_buffer_rsrc_t r3 = tile::buffer_rsrc(gv + (size_t)key0 * DV, left * DV * 2);
 #pragma unroll
         for (int i = 0; i < C::kKLoads; ++i) {
-            const int c = tid + i * kThreads;
-            const int key = min(key0 + c / (D / 8), last_key);
-            const int ch = c % (D / 8);
-            rk1[i] = *(const u32x4*)(gk1 + (size_t)key * D + ch * 8);
-            rk2[i] = *(const u32x4*)(gk2 + (size_t)key * D + ch * 8);
+            rk1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, k_voff[i], 0, 0));
+            rk2[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, k_voff[i], 0, 0));
         }
 #pragma unroll
-        for (int i = 0; i < C::kVLoads; ++i) {
-            const int c = tid + i * kThreads;
-            const int key = min(key0 + c / (DV / 8), last_key);
-            const int ch = c % (DV / 8);
-            rv[i] = *(const u32x4*)(gv + (size_t)key * DV + ch * 8);
-        }
+        for (int i = 0; i < C::kVLoads; ++i)
+            rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r3, v_voff[i], 0, 0));
     };
 
     auto store_tile = [&](int buf) {
