@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 # MI355X published peaks: dense bf16 MFMA and HBM3E bandwidth
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_VALU_TFLOPS = 157.3  # the fp32 kernel runs on the vector ALUs
 PEAK_HBM_GBS = 8000.0
 METRIC = "DiffAttn fwd TFLOP/s (prefill) and KV GB/s (decode), % of roofline"
 
@@ -381,6 +382,8 @@ def main():
     flops = w.exec_flops()
     value = flops / (wall_ms * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
+    # the fp32 workload runs on the vector ALUs, the bf16 ones on the MFMA
+    peak = PEAK_F32_VALU_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -400,12 +403,13 @@ def main():
         "tokens_per_s": round(w.B * w.nq / (wall_ms * 1e-3), 1),
         "formula_tflops": round(w.formula_flops() / (wall_ms * 1e-3) / 1e12, 2),
         "roofline": {
-            "bound": "mfma",
-            "kernel": "prefill_bf16_kernel",
+            "bound": "alu" if w.dtype == "f32" else "mfma",
+            "kernel": ("prefill_f32_kernel" if w.dtype == "f32" else
+                       "prefill_bf16_wide_kernel" if w.d == 128 else "prefill_bf16_kernel"),
             "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": _traffic("prefill_bf16_kernel") if w.name == "causal_prefill_bf16" else None,
             "launch_ms": round(kern_ms, 4),
             "flops_per_launch": flops,
