@@ -177,16 +177,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
         for (int c = 0; c < NVB; ++c) dp = mfma(rd_row(sv_, VS, kr, 16 * c, lh), df[c], dp);
         float p[16], w[16];
+        // the mask is needed only where the tile meets the diagonal or a
+        // ragged end (a wave-uniform test; elsewhere every pair is visible)
+        const int qw0 = __builtin_amdgcn_readfirstlane(qt * 64 + qb * 32);
+        const bool full = qw0 + 31 < a.Nq && kt * 32 + 31 < a.Nk && (!CAUSAL || kt * 32 + 31 <= qw0);
+        auto probs = [&](auto masked) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kt * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
-            const bool ok = qok && key < a.Nk && (!CAUSAL || key <= qrow);
-            float x = fmaf(s[r], sl2, -lse2);
-            asm volatile("" : "+v"(x));  // formed for every lane (no branch)
-            p[r] = __builtin_amdgcn_exp2f(ok ? x : -INFINITY);
-            w[r] = p[r] * dp[r];
-            dsum += w[r];
-        }
+            for (int r = 0; r < 16; ++r) {
+                float x = fmaf(s[r], sl2, -lse2);
+                if constexpr (decltype(masked)::value) {
+                    const int key = kt * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+                    const bool ok = qok && key < a.Nk && (!CAUSAL || key <= qrow);
+                    asm volatile("" : "+v"(x));  // formed for every lane (no branch)
+                    x = ok ? x : -INFINITY;
+                }
+                p[r] = __builtin_amdgcn_exp2f(x);
+                w[r] = p[r] * dp[r];
+                dsum += w[r];
+            }
+        };
+        if (full)
+            probs(std::false_type{});
+        else
+            probs(std::true_type{});
         bf16x8 pp[2], pw[2];
         pack(p, pp);
         pack(w, pw);
@@ -366,23 +379,38 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         for (int r = 0; r < 16; ++r) trow[r] = sr[16 * (r >> 3) + 8 * lh + (r & 7)];
         __builtin_amdgcn_sched_barrier(0);
         float wd[16], d1[16], d2[16];
+        // the mask is needed only where the tile meets the diagonal or a
+        // ragged end (a wave-uniform test; elsewhere every pair is visible)
+        const int kw0 = __builtin_amdgcn_readfirstlane(kt * 128 + wave * 32);
+        const bool full = kw0 + 31 < a.Nk && qt * 32 + 31 < a.Nq && (!CAUSAL || kw0 + 31 <= qt * 32);
+        auto probs = [&](auto masked) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
-            const int q = qt * 32 + qi;
-            const bool ok = kok && q < a.Nq && (!CAUSAL || key <= q);
-            const float4 t = trow[r];
-            // masked pairs take exp2(-inf) = 0; the arguments are formed for
-            // every lane (the empty asm keeps the compiler from moving them,
-            // and the row-term read, into a branch per element)
-            float x1 = fmaf(s1[r], sl2, -t.x), x2 = fmaf(s2[r], sl2, -t.y);
-            asm volatile("" : "+v"(x1), "+v"(x2));
-            const float p1 = __builtin_amdgcn_exp2f(ok ? x1 : -INFINITY);
-            const float p2 = __builtin_amdgcn_exp2f(ok ? x2 : -INFINITY);
-            wd[r] = p1 - lam * p2;
-            d1[r] = p1 * (dp[r] - t.z);
-            d2[r] = -lam * p2 * (dp[r] - t.w);
-        }
+            for (int r = 0; r < 16; ++r) {
+                const float4 t = trow[r];
+                float x1 = fmaf(s1[r], sl2, -t.x), x2 = fmaf(s2[r], sl2, -t.y);
+                if constexpr (decltype(masked)::value) {
+                    const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
+                    const int q = qt * 32 + qi;
+                    const bool ok = kok && q < a.Nq && (!CAUSAL || key <= q);
+                    // masked pairs take exp2(-inf) = 0; the arguments are formed
+                    // for every lane (the empty asm keeps the compiler from
+                    // moving them, and the row-term read, into a branch per
+                    // element)
+                    asm volatile("" : "+v"(x1), "+v"(x2));
+                    x1 = ok ? x1 : -INFINITY;
+                    x2 = ok ? x2 : -INFINITY;
+                }
+                const float p1 = __builtin_amdgcn_exp2f(x1);
+                const float p2 = __builtin_amdgcn_exp2f(x2);
+                wd[r] = p1 - lam * p2;
+                d1[r] = p1 * (dp[r] - t.z);
+                d2[r] = -lam * p2 * (dp[r] - t.w);
+            }
+        };
+        if (full)
+            probs(std::false_type{});
+        else
+            probs(std::true_type{});
         bf16x8 pwd[2], pd1[2], pd2[2];
         pack(wd, pwd);
         pack(d1, pd1);
