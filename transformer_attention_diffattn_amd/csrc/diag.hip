@@ -72,11 +72,19 @@ __global__ __launch_bounds__(kBwdThreads) void diag_rowmax_kernel(DiagArgs a) {
         const uint16_t* kt_ = sk[buf][map];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s = mfma(rd_row(kt_, KS, swap23(l32), 16 * kb, lh), qf[kb], s);
+        // the mask is needed only where the tile meets the diagonal or the
+        // ragged end (a wave-uniform test; elsewhere every key is visible)
+        const int qw0 = __builtin_amdgcn_readfirstlane(qt * 64 + qb * 32);
+        if (kt * 32 + 31 < a.Nk && (!CAUSAL || kt * 32 + 31 <= qw0)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kt * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
-            const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
-            m = fmaxf(m, ok ? s[r] : -INFINITY);
+            for (int r = 0; r < 16; ++r) m = fmaxf(m, s[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kt * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+                const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
+                m = fmaxf(m, ok ? s[r] : -INFINITY);
+            }
         }
         if (more) {
             t1.store(sk[buf ^ 1][0]);
