@@ -24,7 +24,7 @@
 //   waves share each SIMD; a wave waiting on LDS or on the barrier then
 //   leaves the SIMD to the other.  Waves w and w + 4 run on the same SIMD, one
 //   per map.  K1, K2 and V stream through an 8-stage LDS ring in tiles of 32
-//   keys, loaded 6 tiles ahead of use; each wave reads the K tile of its own
+//   keys, loaded 5 tiles ahead of use; each wave reads the K tile of its own
 //   map and the shared V tile.  The main loop is unrolled over one turn of
 //   the ring, so every stage address is an instruction's immediate offset
 //   (K and V sit in two rings of that depth, each under the 64 KB reach of
