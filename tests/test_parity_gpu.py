@@ -117,6 +117,22 @@ def test_prefill_many_items_per_workgroup(d, dv, B, H, nq, nk, causal, pre_norm)
     assert_close(out, ref, w.torch_dtype, f"d{d} B{B} H{H} nq{nq} nk{nk} causal={causal}")
 
 
+# Heavy-tailed inputs near cancellation: Student-t (3 degrees of freedom,
+# unit variance) queries, keys and values, causal, lambda drawn U(0.2, 0.9)
+# per head.  Rows that see only a few keys and whose two maps pick the same
+# key leave D = O1/l1 - lambda O2/l2 with a small spread over the channels,
+# which the GroupNorm scales back up: the bf16 rounding of the probabilities
+# is tested hardest here (llmbytes.dev, "How Differential Attention Cancels
+# Common-Mode Noise", step 4).
+@pytest.mark.parametrize("d,dv", [(128, 256), (64, 128), (32, 64)], ids=lambda v: str(v))
+@pytest.mark.parametrize("B,H,n", [(2, 16, 700), (2, 40, 257)], ids=lambda v: str(v))
+def test_prefill_student_t_near_cancellation(d, dv, B, H, n):
+    w = _custom(B, H, n, n, d, dv, "bf16", True, seed=B * 1000 + H + n + d,
+                dist="student_t3", lam=("uniform", 0.2, 0.9))
+    out, ref = _run_prefill_full_compare(w)
+    assert_close(out, ref, w.torch_dtype, f"student-t d{d} B{B} H{H} n{n}")
+
+
 def test_tiny_noncausal_f32_workload():
     w = workloads.get("tiny_noncausal_f32")
     out, ref = _run_prefill_full_compare(w)

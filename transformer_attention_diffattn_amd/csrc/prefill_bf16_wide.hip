@@ -155,21 +155,28 @@ __device__ __forceinline__ void maybe_rescale(float mx, float& m, float& l, f32x
     }
 }
 
-// Probabilities of one map: p = 2^(s * scale - base), summed into l and
-// packed to bf16 B operands (registers 8kb .. 8kb+7 per 16 keys).
+// Probabilities of one map: p = 2^(s * scale - base), packed to bf16 B
+// operands (registers 8kb .. 8kb+7 per 16 keys) and summed into l.  The sum
+// is taken over the rounded values that enter P.V (a dot product of each
+// packed pair with (1, 1)), so O / l stays an exact weighted mean of V.
 __device__ __forceinline__ void probabilities(const f32x16& s, float sl2, float base, float& l,
                                               bf16x8 (&pb)[2]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float sum0 = 0.f, sum1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kb + e], sl2, -base));
-            if (e & 1)
-                sum1 += p;
+        for (int e = 0; e < 8; e += 2) {
+            const float pa = __builtin_amdgcn_exp2f(fmaf(s[8 * kb + e], sl2, -base));
+            const float pc = __builtin_amdgcn_exp2f(fmaf(s[8 * kb + e + 1], sl2, -base));
+            const bf16x2 pr = {(__bf16)pa, (__bf16)pc};
+            pb[kb][e] = pr[0];
+            pb[kb][e + 1] = pr[1];
+            if (e & 2)
+                sum1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum1, false);
             else
-                sum0 += p;
-            pb[kb][e] = (__bf16)p;
+                sum0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum0, false);
         }
     }
     l += sum0 + sum1;
