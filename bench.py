@@ -1,28 +1,38 @@
 #!/usr/bin/env python3
 """Benchmark of the Differential Attention forward operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--legs LIST]
 
 One step is one fused prefill launch over the whole batch of the headline
-workload (causal_prefill_bf16: B4 H16 N2048, d64, dv128, bf16, causal), i.e.
-operand staging, both score contractions, both online softmaxes, both P.V
+workload (long_needles_bf16: B1 H16 N32768, d64, dv128, bf16, causal, 8
+planted needles per head -- the largest prefill workload), i.e. operand
+staging, both score contractions, both online softmaxes, both P.V
 contractions and the subtraction + GroupNorm epilogue.  Inputs are synthetic,
 seeded, and resident in HBM before timing starts.  The throughput counts
 4 (d + dv) flops per unmasked (query, key) pair (two Q.K^T and two P.V).
 
-The same run also times the decode kernels (split-K partials + merge) on the
-decode workload (B64 H32, one query against an 8192-entry KV cache) and
-reports them in "decode" as GB/s of algorithmic cache traffic, times the
-backward (diffattn_bwd after the training forward) on the headline workload
-("backward", TFLOP/s at 12 d + 4 dv flops per unmasked pair: both score maps
-recomputed, one shared dP, dV, dK1, dK2, dQ1, dQ2), runs the map
-diagnostics on the 32K needle workload ("diagnostics": the row-max sweep at
-4 d flops per unmasked pair, the needle weights, and the values they give on
-those synthetic inputs), times the prefill with Q and K quantised to E4M3
-("fp8_qk"), times the fused Q/K/V projection that produces the headline's
-inputs from d_model = H dv hidden states ("qkv_proj"), and times the fp64 CPU
-oracle on a bounded sample of
-the headline workload ("cpu_baseline").
+Legs (--legs, comma-separated; default all), each timed with events on the
+launch stream and reported with its own roofline block:
+
+  peaks               microbenchmarks: dense bf16 MFMA rate, streaming HBM
+                      read rate, v_exp_f32 and v_fma_f32 rates; every
+                      roofline block also reports its fraction of these
+                      measured peaks, beside the published ones;
+  causal_prefill_bf16, large_head_bf16
+                      the other two bf16 prefill workloads (B4 H16 N2048
+                      d64; B2 H32 N8192 d128 dv256 Student-t, lambda 0.95);
+  decode              the decode kernel on the decode workload (B64 H32, one
+                      query against an 8192-entry KV cache, one split per
+                      (batch, head)), GB/s of algorithmic cache traffic;
+  decode_split        the same with 4 splits per (batch, head): partials
+                      plus the merge kernel;
+  backward            diffattn_bwd after the training forward on
+                      causal_prefill_bf16 (12 d + 4 dv flops per pair);
+  fp8                 the prefill with Q and K as E4M3 on causal_prefill_bf16;
+  proj                the fused Q/K/V projection for causal_prefill_bf16;
+  diag                the map diagnostics on the 32K needle workload;
+  cpu                 the fp64 CPU oracle on a bounded sample of the headline
+                      workload ("cpu_baseline").
 
 Prints one JSON line on stdout.
 """
@@ -42,10 +52,15 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_VALU_TFLOPS = 157.3  # the fp32 kernel runs on the vector ALUs
 PEAK_HBM_GBS = 8000.0
 METRIC = "DiffAttn fwd TFLOP/s (prefill) and KV GB/s (decode), % of roofline"
+HEADLINE = "long_needles_bf16"
+ALL_LEGS = ["peaks", "large_head_bf16", "causal_prefill_bf16", "decode", "decode_split",
+            "backward", "fp8", "proj", "diag", "cpu"]
+DECODE_SPLITS = 4  # the decode_split leg
 
 
 def _events_time(fn, steps: int):
-    """Runs fn() `steps` times between two events on the current stream; returns ms per call."""
+    """Runs fn() `steps` times between two events on the current stream (the
+    stream the library launches on); returns ms per call."""
     import torch
 
     start = torch.cuda.Event(enable_timing=True)
@@ -58,7 +73,15 @@ def _events_time(fn, steps: int):
     return start.elapsed_time(stop) / steps
 
 
-def bench_prefill(w, steps: int, warmup: int):
+def prefill_kernel_name(w) -> str:
+    import transformer_attention_diffattn_amd as da
+
+    return da.prefill_kernel_name(w.d, w.dv, w.dtype)
+
+
+def bench_prefill(w, steps: int, warmup: int, wall: bool = True):
+    """(wall-clock ms per step over exactly `steps` steps between
+    synchronisations, or None; event-timed ms per launch)."""
     import torch
 
     import transformer_attention_diffattn_amd as da
@@ -74,19 +97,120 @@ def bench_prefill(w, steps: int, warmup: int):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # wall clock over exactly `steps` steps, bracketed by synchronisations
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    # per-launch device time from events on the launch stream
+    wall_ms = None
+    if wall:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     kern_ms = _events_time(step, steps)
     del x, out
+    torch.cuda.empty_cache()
     return wall_ms, kern_ms
 
 
-def bench_decode(w, steps: int, warmup: int):
+def roofline(bound, kernel, achieved, peak, unit, measured_peak=None, traffic=None, **extra):
+    """One roofline block: achieved against the published peak, and against
+    the rate the microbenchmarks measured on this GPU when known."""
+    r = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
+         "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic}
+    if measured_peak:
+        r["measured_peak"] = round(measured_peak, 1)
+        r["frac_of_measured"] = round(achieved / measured_peak, 4)
+    r.update(extra)
+    return r
+
+
+def _peaks_lib():
+    import ctypes
+
+    import transformer_attention_diffattn_amd as da
+
+    path = os.path.join(os.path.dirname(da.library_path()), "libdiffattn_peaks.so")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.peaks_mfma_bf16.argtypes = [vp, i32, i32, vp]
+    lib.peaks_read_bw.argtypes = [vp, i64, vp, i32, vp]
+    lib.peaks_vector_rate.argtypes = [vp, i32, i32, i32, vp]
+    for f in (lib.peaks_mfma_bf16, lib.peaks_read_bw, lib.peaks_vector_rate,
+              lib.peaks_mfma_chains, lib.peaks_vector_chains):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def measure_peaks():
+    """Rates of the roofline microbenchmarks (csrc/peaks.hip) on this GPU."""
+    import torch
+
+    lib = _peaks_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(launch, reps=5):
+        for _ in range(2):
+            if launch() != 0:
+                raise RuntimeError("microbenchmark launch failed")
+        torch.cuda.synchronize()
+        return min(_events_time(launch, 3) for _ in range(reps))
+
+    out = {"compute_units": cus}
+    # bf16 MFMA: 8 blocks of 4 waves per CU (two waves per SIMD)
+    blocks, iters = cus * 8, 4096
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    ms = timed(lambda: lib.peaks_mfma_bf16(sink.data_ptr(), blocks, iters, stream))
+    flops = blocks * 4 * iters * lib.peaks_mfma_chains() * 32768
+    out["mfma_bf16_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    # the shader clock the matrix cores ran at: 4096 bf16 flops per CU and cycle
+    out["mfma_clock_ghz"] = round(flops / (ms * 1e-3) / (cus * 4096) / 1e9, 3)
+    # streaming reads of 4 GiB, each byte once
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    rblocks = cus * 8
+    rsink = torch.empty(rblocks * 512, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: lib.peaks_read_bw(src.data_ptr(), nbytes // 16, rsink.data_ptr(), rblocks,
+                                         stream), reps=3)
+    out["hbm_read_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del src, rsink
+    # vector rates: 8 blocks of 4 waves per CU, 8 independent chains per lane
+    vblocks, viters = cus * 8, 2048
+    per = vblocks * 256 * viters * lib.peaks_vector_chains()
+    for name, use_fma in (("exp", 0), ("fma", 1)):
+        ms = timed(lambda: lib.peaks_vector_rate(sink.data_ptr(), vblocks, viters, use_fma, stream))
+        rate = per / (ms * 1e-3)
+        out[f"v_{name}_f32_per_cu_clk"] = round(rate / cus / (out["mfma_clock_ghz"] * 1e9), 2)
+    out["note"] = ("lanes per CU and shader cycle, at the clock the MFMA test ran at; "
+                   "v_fma_f32 counts one instruction per lane")
+    del sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def device_info():
+    """CU count and the shader clock range as the runtime reports them."""
+    import subprocess
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count}
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        agent = [blk for blk in txt.split("Agent ") if "gfx950" in blk]
+        if agent:
+            for line in agent[0].splitlines():
+                if "Max Clock Freq." in line:
+                    info["max_clock_mhz"] = int(line.split(":")[1].split("(")[0])
+                    break
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    return info
+
+
+def bench_decode(w, steps: int, warmup: int, splits: int = 0):
+    """ms per decode call on workload w (splits = 0: the library's default)."""
     import torch
 
     import transformer_attention_diffattn_amd as da
@@ -94,7 +218,8 @@ def bench_decode(w, steps: int, warmup: int):
 
     x = workloads.make_decode(w, device="cuda")
     out = torch.empty((w.B, w.H, w.dv), dtype=w.torch_dtype, device="cuda")
-    splits = da.decode_default_splits(w.B, w.H, w.nk, w.d, w.dv)
+    if splits <= 0:
+        splits = da.decode_default_splits(w.B, w.H, w.nk, w.d, w.dv)
     ws_bytes = da.decode_workspace_size(w.B, w.H, w.nk, w.d, w.dv, splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
@@ -233,12 +358,13 @@ def cpu_baseline(w, budget_s: float = 30.0):
 COPY_BYTES = 1 << 30
 
 
-def _traffic(kernel: str):
+def _traffic(kernel: str, workload: str):
     """Scaled HBM bytes per launch from the committed rocprofv3 counter summary
-    of this kernel, or None when there is none or the kernel source changed."""
+    of this kernel on this workload, or None when there is none or the
+    kernel source changed since it was taken."""
     import profile_kernels
 
-    rec = profile_kernels.load(kernel)
+    rec = profile_kernels.load(kernel, workload)
     return None if rec is None else rec["traffic_bytes_per_launch"]
 
 
@@ -336,19 +462,39 @@ def bench_proj(w, steps: int, warmup: int):
     return ms, lib_ms, flops
 
 
+def prefill_record(w, wall_ms, kern_ms, mpk):
+    """Throughput of one prefill workload and its roofline block."""
+    flops = w.exec_flops()
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    f32 = w.dtype == "f32"
+    kernel = prefill_kernel_name(w)
+    rec = {
+        "workload": w.name,
+        "ms_per_launch": round(kern_ms, 4),
+        "tflops": round(achieved, 2),
+        "tokens_per_s": round(w.B * w.nq / (kern_ms * 1e-3), 1),
+        "formula_tflops": round(w.formula_flops() / (kern_ms * 1e-3) / 1e12, 2),
+        "roofline": roofline(
+            "alu" if f32 else "mfma", kernel, achieved,
+            PEAK_F32_VALU_TFLOPS if f32 else PEAK_BF16_TFLOPS, "TFLOP/s",
+            None if f32 else mpk.get("mfma_bf16_tflops"), _traffic(kernel, w.name),
+            launch_ms=round(kern_ms, 4), flops_per_launch=flops),
+    }
+    if wall_ms is not None:
+        rec["wall_ms_per_step"] = round(wall_ms, 4)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     # a few hundred launches let the GPU reach its steady clocks before timing
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="causal_prefill_bf16")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
-    ap.add_argument("--no-diag", action="store_true", help="skip the diagnostics leg")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 query/key leg")
-    ap.add_argument("--no-proj", action="store_true", help="skip the Q/K/V projection leg")
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--legs", default=",".join(ALL_LEGS),
+                    help="comma-separated legs to run besides the headline (or 'none'): "
+                         + ", ".join(ALL_LEGS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain fp32 copy of 1 GiB (3 times), the reference the "
                          "HBM byte counters are scaled by")
@@ -358,6 +504,11 @@ def main():
         print("bench.py measures one GPU: this operator is built and timed on a single "
               "MI355X (multi-GPU sharding is a design note only); run with --gpus 1.",
               file=sys.stderr)
+        sys.exit(2)
+    legs = [] if args.legs == "none" else [x for x in args.legs.split(",") if x]
+    unknown = [x for x in legs if x not in ALL_LEGS]
+    if unknown:
+        print(f"unknown legs {unknown}; known: {ALL_LEGS}", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -378,12 +529,22 @@ def main():
     if w.kind != "prefill":
         print("--workload must name a prefill workload", file=sys.stderr)
         sys.exit(2)
+
+    mpk = measure_peaks() if "peaks" in legs else {}
+
+    # the other prefill workloads first (each with the same warm-up and step
+    # counts), then the headline
+    prefill_legs = {}
+    for name in ("large_head_bf16", "causal_prefill_bf16"):
+        if name in legs and name != w.name:
+            wl = workloads.get(name)
+            _, lms = bench_prefill(wl, args.steps, args.warmup, wall=False)
+            prefill_legs[name] = prefill_record(wl, None, lms, mpk)
+
     wall_ms, kern_ms = bench_prefill(w, args.steps, args.warmup)
     flops = w.exec_flops()
     value = flops / (wall_ms * 1e-3) / 1e12
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-    # the fp32 workload runs on the vector ALUs, the bf16 ones on the MFMA
-    peak = PEAK_F32_VALU_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    head = prefill_record(w, wall_ms, kern_ms, mpk)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -402,27 +563,24 @@ def main():
                    "global_batch": w.B, "parallelism": "single GPU"},
         "tokens_per_s": round(w.B * w.nq / (wall_ms * 1e-3), 1),
         "formula_tflops": round(w.formula_flops() / (wall_ms * 1e-3) / 1e12, 2),
-        "roofline": {
-            "bound": "alu" if w.dtype == "f32" else "mfma",
-            "kernel": ("prefill_f32_kernel" if w.dtype == "f32" else
-                       "prefill_bf16_wide_kernel" if w.d == 128 else "prefill_bf16_kernel"),
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": _traffic("prefill_bf16_kernel") if w.name == "causal_prefill_bf16" else None,
-            "launch_ms": round(kern_ms, 4),
-            "flops_per_launch": flops,
-        },
+        "roofline": head["roofline"],
+        "device": device_info(),
     }
+    if mpk:
+        rec["peaks"] = mpk
+    if prefill_legs:
+        rec["prefill_legs"] = prefill_legs
 
-    if not args.no_decode:
-        wd = workloads.get("decode_bf16")
-        dec_steps = max(5, args.steps // 5)
-        dms, splits, ws_bytes = bench_decode(wd, dec_steps, max(2, args.warmup // 30))
-        nbytes = wd.algorithmic_bytes()
+    wd = workloads.get("decode_bf16")
+    nbytes = wd.algorithmic_bytes()
+    for leg, want in (("decode", 0), ("decode_split", DECODE_SPLITS)):
+        if leg not in legs:
+            continue
+        dms, splits, ws_bytes = bench_decode(wd, max(5, args.steps // 5), max(2, args.warmup // 10),
+                                             splits=want)
         gbs = nbytes / (dms * 1e-3) / 1e9
-        rec["decode"] = {
+        kern = "decode_partial_kernel" + (" + decode_merge_kernel" if splits > 1 else "")
+        rec[leg] = {
             "workload": wd.name,
             "value": round(gbs, 1),
             "unit": "GB/s",
@@ -430,70 +588,69 @@ def main():
             "tokens_per_s": round(wd.B / (dms * 1e-3), 1),
             "splits": splits,
             "workspace_bytes": ws_bytes,
-            "roofline": {"bound": "hbm", "kernel": "decode_partial_kernel (+ merge)",
-                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": _traffic("decode_partial_kernel"),
-                         "bytes_per_call": nbytes},
+            "roofline": roofline("hbm", kern, gbs, PEAK_HBM_GBS, "GB/s",
+                                 mpk.get("hbm_read_gbs"),
+                                 _traffic("decode_partial_kernel", wd.name) if splits == 1 else None,
+                                 bytes_per_call=nbytes),
         }
 
-    if not args.no_backward and w.dtype == "bf16" and (w.d, w.dv) in ((32, 64), (64, 128)):
-        bms, tfms = bench_backward(w, max(5, args.steps // 5), max(3, args.warmup // 20))
-        pairs = flops / (4 * (w.d + w.dv))
-        bflops = pairs * (12 * w.d + 4 * w.dv)
+    w2 = workloads.get("causal_prefill_bf16")
+    f2 = w2.exec_flops()
+    pairs2 = f2 / (4 * (w2.d + w2.dv))
+    if "backward" in legs:
+        bms, tfms = bench_backward(w2, max(5, args.steps // 5), max(3, args.warmup // 20))
+        bflops = pairs2 * (12 * w2.d + 4 * w2.dv)
         btf = bflops / (bms * 1e-3) / 1e12
         rec["backward"] = {
-            "workload": w.name,
+            "workload": w2.name,
             "value": round(btf, 2),
             "unit": "TFLOP/s",
             "ms_per_call": round(bms, 4),
             "flops_per_call": int(bflops),
             "fwd_train_ms": round(tfms, 4),
-            "roofline": {"bound": "mfma", "kernel": "bwd_prep + bwd_dq + bwd_dkdv + bwd_dlam",
-                         "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(btf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None},
+            "roofline": roofline("mfma", "bwd_prep + bwd_dq + bwd_dkdv + bwd_dlam", btf,
+                                 PEAK_BF16_TFLOPS, "TFLOP/s", mpk.get("mfma_bf16_tflops")),
         }
 
-    if not args.no_fp8 and w.dtype == "bf16" and (w.d, w.dv) == (64, 128):
-        fms, bms16 = bench_fp8(w, max(10, args.steps // 3), max(20, args.warmup // 5))
-        pairs = flops / (4 * (w.d + w.dv))
+    if "fp8" in legs:
+        fms, bms16 = bench_fp8(w2, max(10, args.steps // 3), max(20, args.warmup // 5))
         # scores on the e4m3 MFMA (peak 2x bf16), P.V on the bf16 one: the
         # peak of this mix is the flops over their time at the two peaks
-        mix_peak = flops / (pairs * (4 * w.d / (2 * PEAK_BF16_TFLOPS) + 4 * w.dv / PEAK_BF16_TFLOPS))
-        ftf = flops / (fms * 1e-3) / 1e12
+        def mix(p):
+            return f2 / (pairs2 * (4 * w2.d / (2 * p) + 4 * w2.dv / p))
+        ftf = f2 / (fms * 1e-3) / 1e12
+        mm = mpk.get("mfma_bf16_tflops")
         rec["fp8_qk"] = {
-            "workload": w.name + " (Q, K as e4m3, per-tensor scales)",
+            "workload": w2.name + " (Q, K as e4m3, per-tensor scales)",
             "value": round(ftf, 2),
             "unit": "TFLOP/s",
             "ms_per_call": round(fms, 4),
             "bf16_ms_per_call_same_run": round(bms16, 4),
             "speedup_vs_bf16": round(bms16 / fms, 3),
-            "roofline": {"bound": "mfma", "kernel": "prefill_fp8qk_kernel",
-                         "achieved": round(ftf, 2), "peak": round(mix_peak, 1),
-                         "unit": "TFLOP/s", "frac": round(ftf / mix_peak, 4),
-                         "traffic": None},
+            "roofline": roofline("mfma", "prefill_fp8qk_kernel", ftf, round(mix(PEAK_BF16_TFLOPS), 1),
+                                 "TFLOP/s", mix(mm) if mm else None,
+                                 _traffic("prefill_fp8qk_kernel", w2.name)),
         }
 
-    if not args.no_proj and w.dtype == "bf16":
-        pms, lms, pflops = bench_proj(w, max(10, args.steps // 3), max(20, args.warmup // 3))
+    if "proj" in legs:
+        pms, lms, pflops = bench_proj(w2, max(10, args.steps // 3), max(20, args.warmup // 3))
         ptf = pflops / (pms * 1e-3) / 1e12
         rec["qkv_proj"] = {
-            "workload": f"{w.name} projections (d_model {w.H * w.dv})",
+            "workload": f"{w2.name} projections (d_model {w2.H * w2.dv})",
             "value": round(ptf, 2),
             "unit": "TFLOP/s",
             "ms_per_call": round(pms, 4),
             "flops_per_call": pflops,
             "library_gemm_ms_no_head_split": round(lms, 4),
-            "roofline": {"bound": "mfma", "kernel": "qkv_proj_kernel", "achieved": round(ptf, 2),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ptf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "roofline": roofline("mfma", "qkv_proj_kernel", ptf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                 mpk.get("mfma_bf16_tflops"),
+                                 _traffic("qkv_proj_kernel", w2.name)),
         }
 
-    if not args.no_diag:
+    if "diag" in legs:
         rec["diagnostics"] = bench_diag(max(3, args.steps // 20))
 
-    if not args.no_cpu:
+    if "cpu" in legs:
         cb = cpu_baseline(w)
         cb["cpu"] = _cpu_model()
         rec["cpu_baseline"] = cb

@@ -7,20 +7,29 @@
 
 (DIR: where rocprofv3 writes its raw output, default prof_out/.)
 
-`run` starts three rocprofv3 child processes over bench.py (each with its own
-time limit, from /tmp with TMPDIR=/tmp):
+`run` starts rocprofv3 child processes over bench.py (each with its own time
+limit, from /tmp with TMPDIR=/tmp):
 
-  1. --kernel-trace --stats          per-kernel launch durations;
-  2. --pmc FETCH_SIZE                 HBM read KiB per dispatch;
-  3. --pmc WRITE_SIZE                 HBM write KiB per dispatch;
+  trace          --kernel-trace --stats over the default bench.py command:
+                 per-dispatch launch durations;
+  fetch_*, write_*
+                 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (HBM read and write
+                 KiB per dispatch), each over two short bench.py commands that
+                 between them run every measured kernel on its workload, one
+                 workload per kernel name in each command.
 
-the two counter passes also run bench.py's plain 1 GiB copy first, whose
-counter readings give the scale factors (bytes the copy really moves divided by
-what the counter reports).  `summarize` (also done at the end of `run`) writes
-one short text summary per measured kernel into profiles/, with the commands,
+The counter passes also run bench.py's plain 1 GiB copy first, whose counter
+readings give the scale factors (bytes the copy really moves divided by what
+the counter reports).  `summarize` (also done at the end of `run`) writes one
+short text summary per (kernel, workload) into profiles/, with the commands,
 the average launch duration, the scaled per-launch HBM traffic and the sha256
 of the kernel's source at the time.  bench.py reports `traffic` from these
 summaries only while that source is unchanged.
+
+Where one kernel runs on two workloads in the traced command (the head_dim-64
+prefill on the 32K and the 2K workloads), each dispatch is attributed to the
+workload whose event-timed launch in the same run is nearest in log time (the
+two differ by a factor of ~50).
 """
 from __future__ import annotations
 
@@ -29,6 +38,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import subprocess
 import sys
@@ -37,21 +47,43 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "transformer_attention_diffattn_amd", "csrc")
+sys.path.insert(0, ROOT)
 
 # the trace pass runs the default benchmark command itself, so that its
 # average launch durations are those of the reported figures
 BENCH_ARGS: list = []
-# the counter passes need only the headline prefill and the decode launches
-PMC_BENCH_ARGS = ["--steps", "3", "--warmup", "1", "--no-cpu", "--no-backward", "--no-diag",
-                  "--no-proj", "--no-fp8", "--copy-calibration"]
+# counter passes: two short commands; in each, a kernel name runs on one workload
+_PMC_COMMON = ["--steps", "3", "--warmup", "1", "--copy-calibration"]
+PMC_BENCHES = {
+    "a": ["--workload", "long_needles_bf16", "--legs", "decode", *_PMC_COMMON],
+    "b": ["--workload", "causal_prefill_bf16", "--legs", "large_head_bf16,fp8,proj,backward",
+          *_PMC_COMMON],
+}
 COPY_BYTES = 1 << 30
 COPY_GRID = COPY_BYTES // 16  # threads of the vectorised copy (4 floats per thread)
+_PREFILL = "prefill_core.h+prefill_bf16.hip"
 
-# kernel -> (workload it runs on in bench.py, its source files joined by "+")
-KERNELS = {
-    "prefill_bf16_kernel": ("causal_prefill_bf16", "prefill_core.h+prefill_bf16.hip"),
-    "decode_partial_kernel": ("decode_bf16", "decode.hip"),
-}
+
+def _wide() -> str:
+    import transformer_attention_diffattn_amd as da
+    return da.prefill_kernel_name(128, 256)
+
+
+def entries():
+    """(kernel, workload, source files joined by '+', counter pass, how bench.py
+    reports its event-timed launch: a path into the JSON line)."""
+    return [
+        ("prefill_bf16_kernel", "long_needles_bf16", _PREFILL, "a", ("roofline", "launch_ms")),
+        ("prefill_bf16_kernel", "causal_prefill_bf16", _PREFILL, "b",
+         ("prefill_legs", "causal_prefill_bf16", "ms_per_launch")),
+        (_wide(), "large_head_bf16", "prefill_twopass.hip", "b",
+         ("prefill_legs", "large_head_bf16", "ms_per_launch")),
+        ("decode_partial_kernel", "decode_bf16", "decode.hip", "a", ("decode", "ms_per_call")),
+        ("prefill_fp8qk_kernel", "causal_prefill_bf16", _PREFILL, "b", ("fp8_qk", "ms_per_call")),
+        ("qkv_proj_kernel", "causal_prefill_bf16", "proj.hip", "b", ("qkv_proj", "ms_per_call")),
+        ("bwd_dq_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
+        ("bwd_dkdv_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
+    ]
 
 
 def source_sha(fnames: str) -> str:
@@ -66,14 +98,15 @@ def source_sha(fnames: str) -> str:
 def _commands(out: str):
     py = sys.executable or "python3"
     bench = os.path.join(ROOT, "bench.py")
-    return {
-        "trace": ["rocprofv3", "--kernel-trace", "--stats", "-T", "-d", os.path.join(out, "trace"),
-                  "-o", "run", "-f", "csv", "--", py, bench, *BENCH_ARGS],
-        "fetch": ["rocprofv3", "--pmc", "FETCH_SIZE", "-d", os.path.join(out, "fetch"), "-o",
-                  "run", "-f", "csv", "--", py, bench, *PMC_BENCH_ARGS],
-        "write": ["rocprofv3", "--pmc", "WRITE_SIZE", "-d", os.path.join(out, "write"), "-o",
-                  "run", "-f", "csv", "--", py, bench, *PMC_BENCH_ARGS],
-    }
+    cmds = {"trace": ["rocprofv3", "--kernel-trace", "--stats", "-T", "-d",
+                      os.path.join(out, "trace"), "-o", "run", "-f", "csv", "--", py, bench,
+                      *BENCH_ARGS]}
+    for key, bargs in PMC_BENCHES.items():
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            sub = f"{ctr.split('_')[0].lower()}_{key}"
+            cmds[sub] = ["rocprofv3", "--pmc", ctr, "-d", os.path.join(out, sub), "-o", "run",
+                         "-f", "csv", "--", py, bench, *bargs]
+    return cmds
 
 
 def run(out: str) -> None:
@@ -85,7 +118,7 @@ def run(out: str) -> None:
         with open(os.path.join(out, f"{name}.log"), "w") as log:
             # SIGKILL at the limit: a counter pass that cannot be collected hangs
             subprocess.run(cmd, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT,
-                           timeout=240, check=True)
+                           timeout=300, check=True)
         print(f"[profile] pass {name} done", flush=True)
     summarize(out)
 
@@ -97,19 +130,40 @@ def _find(out: str, sub: str, suffix: str) -> str:
     return sorted(hits)[0]
 
 
-def _bench_ms_in_trace(out: str, kernel: str):
-    """The per-launch time bench.py measured with events inside the traced run."""
+def _bench_record(out: str):
+    """The JSON line bench.py printed inside the traced run."""
     try:
         with open(os.path.join(out, "trace.log")) as f:
             lines = [l for l in f if l.startswith("{")]
-        rec = json.loads(lines[-1])
+        return json.loads(lines[-1])
     except (OSError, IndexError, ValueError):
         return None
-    if kernel == "prefill_bf16_kernel":
-        return rec["roofline"]["launch_ms"]
-    if kernel == "decode_partial_kernel" and "decode" in rec:
-        return rec["decode"]["ms_per_call"]
-    return None
+
+
+def _dig(rec, path):
+    for k in path or ():
+        if not isinstance(rec, dict) or k not in rec:
+            return None
+        rec = rec[k]
+    return rec
+
+
+def _short(name: str, kernels) -> str:
+    """The library kernel a demangled dispatch name belongs to, else the name."""
+    for k in kernels:
+        if f"{k}<" in name or name == k or f"::{k}" in name or name.startswith(k + "("):
+            return k
+    return name
+
+
+def _trace_durations(out: str, kernels):
+    """Per library kernel: the durations (ns) of its dispatches, in order."""
+    per = defaultdict(list)
+    with open(_find(out, "trace", "kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            k = _short(r["Kernel_Name"], kernels)
+            per[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return per
 
 
 def _kernel_stats(out: str):
@@ -138,49 +192,65 @@ def _calibration(per) -> float:
     return sum(vals) / len(vals)
 
 
-def _short(name: str) -> str:
-    """The library kernel a demangled dispatch name belongs to, else the name."""
-    for k in KERNELS:
-        if f"{k}<" in name or name == k or f"::{k}" in name:
-            return k
-    return name
+def _attribute(durs, centers):
+    """Split durations among workloads by nearest centre in log time.
+    centers: {workload: ms}.  Returns {workload: [ns, ...]}."""
+    got = defaultdict(list)
+    named = {w: c for w, c in centers.items() if c}
+    for d in durs:
+        if not named:
+            break
+        w = min(named, key=lambda k: abs(math.log(d / 1e6) - math.log(named[k])))
+        got[w].append(d)
+    return got
 
 
 def summarize(out: str) -> None:
-    out = os.path.abspath(out)
-    stats = _kernel_stats(out)
-    fetch, write = _counter(out, "fetch"), _counter(out, "write")
-    copy_kib = COPY_BYTES / 1024
-    f_cal, w_cal = _calibration(fetch), _calibration(write)
-    f_factor, w_factor = copy_kib / f_cal, copy_kib / w_cal
-    cmds = _commands(os.path.relpath(out, ROOT))
-    os.makedirs(PROFILES, exist_ok=True)
-    sys.path.insert(0, ROOT)
     import workloads
 
-    for kern, (wname, src) in KERNELS.items():
-        st = stats.get(kern)
-        fv = [v for n, xs in fetch.items() if _short(n) == kern for _, v in xs]
-        wv = [v for n, xs in write.items() if _short(n) == kern for _, v in xs]
-        if st is None or not fv or not wv:
-            print(f"[profile] {kern}: not found, skipped", flush=True)
+    out = os.path.abspath(out)
+    ents = entries()
+    kernels = sorted({e[0] for e in ents}, key=len, reverse=True)
+    durs = _trace_durations(out, kernels)
+    stats = _kernel_stats(out)
+    bench = _bench_record(out)
+    copy_kib = COPY_BYTES / 1024
+    fetch = {k: _counter(out, f"fetch_{k}") for k in PMC_BENCHES}
+    write = {k: _counter(out, f"write_{k}") for k in PMC_BENCHES}
+    cal = {k: (copy_kib / _calibration(fetch[k]), copy_kib / _calibration(write[k]))
+           for k in PMC_BENCHES}
+    cmds = _commands(os.path.relpath(out, ROOT))
+    os.makedirs(PROFILES, exist_ok=True)
+    centers = defaultdict(dict)
+    for kern, wname, _, _, path in ents:
+        centers[kern][wname] = _dig(bench, path) if path else None
+
+    for kern, wname, src, pmc, path in ents:
+        same = [w for w, c in centers[kern].items()]
+        mine = (_attribute(durs.get(kern, []), centers[kern]).get(wname, [])
+                if len(same) > 1 else durs.get(kern, []))
+        fv = [v for n, xs in fetch[pmc].items() if _short(n, kernels) == kern for _, v in xs]
+        wv = [v for n, xs in write[pmc].items() if _short(n, kernels) == kern for _, v in xs]
+        if not mine or not fv or not wv:
+            print(f"[profile] {kern} on {wname}: not found, skipped", flush=True)
             continue
         w = workloads.get(wname)
+        f_factor, w_factor = cal[pmc]
         fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
-        bench_ms = _bench_ms_in_trace(out, kern)
+        bench_ms = _dig(bench, path) if path else None
         traffic = int(round((fk * f_factor + wk * w_factor) * 1024))
         rec = {
-            "kernel": kern, "workload": wname, "calls": int(st["Calls"]),
-            "avg_ns": float(st["AverageNs"]), "min_ns": float(st["MinNs"]),
-            "max_ns": float(st["MaxNs"]),
+            "kernel": kern, "workload": wname, "calls": len(mine),
+            "avg_ns": sum(mine) / len(mine), "min_ns": float(min(mine)),
+            "max_ns": float(max(mine)),
             "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
-            "copy_fetch_kib": f_cal, "copy_write_kib": w_cal,
             "fetch_factor": f_factor, "write_factor": w_factor,
             "traffic_bytes_per_launch": traffic,
-            "algorithmic_bytes_per_launch": w.algorithmic_bytes(),
             "source": src, "source_sha256": source_sha(src),
             "bench_event_ms_in_traced_run": bench_ms,
         }
+        if kern.startswith("prefill") or kern.startswith("decode"):
+            rec["algorithmic_bytes_per_launch"] = w.algorithmic_bytes()
         lines = [
             f"# {kern} on {wname}",
             "",
@@ -190,6 +260,8 @@ def summarize(out: str) -> None:
             "",
         ]
         for name, cmd in cmds.items():
+            if name != "trace" and not name.endswith("_" + pmc):
+                continue
             shown = ["python3" if c == (sys.executable or "python3") else
                      (os.path.relpath(c, ROOT) if c.startswith(ROOT) else c) for c in cmd]
             lines.append(f"- {name}: `{' '.join(shown)}`")
@@ -197,31 +269,29 @@ def summarize(out: str) -> None:
             "",
             "| quantity | value |",
             "|---|---|",
-            f"| launches traced | {rec['calls']} |",
+            f"| launches traced (this workload) | {rec['calls']} |",
             f"| bench.py event-timed launch in the same traced run | "
             f"{'n/a' if bench_ms is None else f'{bench_ms * 1e3:.1f} us'} |",
             f"| average duration | {rec['avg_ns'] / 1e3:.1f} us (min {rec['min_ns'] / 1e3:.1f}, "
             f"max {rec['max_ns'] / 1e3:.1f}) |",
             f"| FETCH_SIZE per dispatch | {fk:,.1f} KiB |",
             f"| WRITE_SIZE per dispatch | {wk:,.1f} KiB |",
-            f"| 1 GiB copy reads as | FETCH {f_cal:,.1f} KiB, WRITE {w_cal:,.1f} KiB |",
-            f"| scale factors | fetch x{f_factor:.4f}, write x{w_factor:.4f} |",
+            f"| scale factors (1 GiB copy) | fetch x{f_factor:.4f}, write x{w_factor:.4f} |",
             f"| HBM traffic per launch (scaled) | {traffic:,} B |",
-            f"| algorithmic bytes per launch | {rec['algorithmic_bytes_per_launch']:,} B |",
-            f"| traffic / algorithmic | {traffic / rec['algorithmic_bytes_per_launch']:.3f} |",
-            "",
-            "All kernels in the traced run:",
-            "",
-            "| kernel | calls | average (us) |",
-            "|---|---|---|",
         ]
+        if "algorithmic_bytes_per_launch" in rec:
+            ab = rec["algorithmic_bytes_per_launch"]
+            lines += [f"| algorithmic bytes per launch | {ab:,} B |",
+                      f"| traffic / algorithmic | {traffic / ab:.3f} |"]
+        lines += ["", "All kernels in the traced run (every workload):", "",
+                  "| kernel | calls | average (us) |", "|---|---|---|"]
         for name, r in stats.items():
             lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} |")
         lines += ["", "```json", json.dumps(rec, indent=1), "```", ""]
-        path = os.path.join(PROFILES, f"{kern}__{wname}.md")
-        with open(path, "w") as f:
+        path_md = os.path.join(PROFILES, f"{kern}__{wname}.md")
+        with open(path_md, "w") as f:
             f.write("\n".join(lines))
-        print(f"[profile] wrote {os.path.relpath(path, ROOT)}", flush=True)
+        print(f"[profile] wrote {os.path.relpath(path_md, ROOT)}", flush=True)
 
 
 # counter groups for the prefill kernel (each fits one pass: <= 8 SQ, <= 2 GRBM)
@@ -241,18 +311,18 @@ def _counter_cmd(out: str, i: int, workload: str):
     py = sys.executable or "python3"
     return ["rocprofv3", "--pmc", *COUNTER_PASSES[i], "-d", os.path.join(out, f"counters{i}"),
             "-o", "run", "-f", "csv", "--", py, os.path.join(ROOT, "bench.py"), "--steps", "3",
-            "--warmup", "1", "--no-cpu", "--no-decode", "--no-backward", "--no-diag", "--no-fp8",
-            "--no-proj", "--workload", workload]
+            "--warmup", "1", "--legs", "none", "--workload", workload]
 
 
 def prefill_kernel_of(workload: str) -> str:
-    """The prefill kernel bench.py runs on `workload` (head_dim 128: the wide one)."""
-    sys.path.insert(0, ROOT)
+    """The prefill kernel bench.py runs on `workload`."""
+    import transformer_attention_diffattn_amd as da
     import workloads
-    return "prefill_bf16_wide_kernel" if workloads.get(workload).d == 128 else "prefill_bf16_kernel"
+    w = workloads.get(workload)
+    return da.prefill_kernel_name(w.d, w.dv, w.dtype)
 
 
-def counters(out: str, workload: str = "causal_prefill_bf16") -> None:
+def counters(out: str, workload: str = "long_needles_bf16") -> None:
     """Runs the counter passes of COUNTER_PASSES over bench.py on one workload."""
     out = os.path.abspath(out)
     os.makedirs(out, exist_ok=True)
@@ -303,8 +373,7 @@ def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
         derived["exp (TRANS) instructions per MFMA"] = (
             vals.get("SQ_INSTS_VALU_TRANS_F32", 0) / vals["SQ_INSTS_MFMA"])
         derived["LDS instructions per MFMA"] = vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"]
-    src = {"prefill_bf16_wide_kernel": "prefill_bf16_wide.hip"}.get(
-        kernel, KERNELS.get(kernel, (None, "prefill_core.h+prefill_bf16.hip"))[1])
+    src = ([e[2] for e in entries() if e[0] == kernel] or [_PREFILL])[0]
     lines = [f"# {kernel} on {workload}: SQ counters per dispatch", "",
              "Commands (from /tmp, TMPDIR=/tmp; written by "
              f"`python3 profile_kernels.py counters --workload {workload}`):", ""]
@@ -327,19 +396,20 @@ def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
     print(f"[profile] wrote {path}", flush=True)
 
 
-def load(kernel: str):
-    """The stored summary of `kernel`, or None if absent or its source changed."""
-    if kernel not in KERNELS:
+def load(kernel: str, workload: str):
+    """The stored summary of `kernel` on `workload`, or None if absent or the
+    kernel's source changed since it was taken."""
+    ent = [e for e in entries() if e[0] == kernel and e[1] == workload]
+    if not ent:
         return None
-    wname, src = KERNELS[kernel]
-    path = os.path.join(PROFILES, f"{kernel}__{wname}.md")
+    path = os.path.join(PROFILES, f"{kernel}__{workload}.md")
     try:
         with open(path) as f:
             text = f.read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
-    if rec.get("source_sha256") != source_sha(src):
+    if rec.get("source_sha256") != source_sha(ent[0][2]):
         return None
     return rec
 
@@ -348,7 +418,7 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("action", choices=["run", "summarize", "counters", "counters-summarize"])
     ap.add_argument("--out", default=os.path.join(ROOT, "prof_out"))
-    ap.add_argument("--workload", default="causal_prefill_bf16")
+    ap.add_argument("--workload", default="long_needles_bf16")
     ap.add_argument("--profiles-dir", default=PROFILES,
                     help="where summaries go (on a remote GPU box: a folder that is copied back)")
     a = ap.parse_args()

@@ -97,6 +97,38 @@ def test_prefill_pre_norm_output(dtype):
     assert_close(out, ref, w.torch_dtype, "pre-norm D")
 
 
+# head_dim 128: rectangular non-causal shapes, the pre-norm output, and
+# lambda outside [0, 1] (negative, zero, and above 1, where the exchanged
+# weights are scaled down to stay in fp16 range)
+@pytest.mark.parametrize("nq,nk", [(70, 300), (300, 5), (1, 513), (200, 64)])
+def test_prefill_rectangular_noncausal_d128(nq, nk):
+    w = _custom(1, 2, nq, nk, 128, 256, "bf16", False, seed=nq * 5 + nk)
+    out, ref = _run_prefill_full_compare(w)
+    assert_close(out, ref, w.torch_dtype, f"d128 nq{nq} nk{nk}")
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_prefill_pre_norm_output_d128(causal):
+    w = _custom(1, 3, 230, 230, 128, 256, "bf16", causal, seed=78)
+    out, ref = _run_prefill_full_compare(w, pre_norm=True)
+    assert_close(out, ref, w.torch_dtype, "pre-norm D, d128")
+
+
+@pytest.mark.parametrize("dims", da.SUPPORTED_DIMS, ids=lambda t: f"d{t[0]}")
+def test_prefill_lambda_outside_unit_interval(dims):
+    d, dv = dims
+    w = _custom(1, 4, 190, 190, d, dv, "bf16", True, seed=79)
+    x = workloads.make_prefill(w, device="cpu")
+    x["lam"] = torch.tensor([-0.7, 0.0, 1.6, 3.0], dtype=torch.float32)
+    xg = _to(x)
+    for pre in (True, False):
+        out = da.fwd(xg["q1"], xg["q2"], xg["k1"], xg["k2"], xg["v"], xg["lam"], causal=True,
+                     pre_norm=pre)
+        ref = oracle.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=True,
+                         pre_norm=pre)
+        assert_close(out, ref, torch.bfloat16, f"d{d} lambda outside [0, 1], pre_norm={pre}")
+
+
 # More (query tile, head) items than compute units: each workgroup of the
 # bf16 kernel runs several items in turn, reusing its LDS ring, and the items
 # it gets differ in length (causal) or are very short (few keys).
@@ -110,6 +142,11 @@ def test_prefill_pre_norm_output(dtype):
     (32, 64, 2, 64, 700, 700, False, False),
     (32, 64, 1, 260, 97, 97, True, True),
     (32, 64, 3, 100, 257, 257, True, False),
+    (128, 256, 1, 300, 40, 40, True, False),
+    (128, 256, 2, 64, 700, 700, True, False),
+    (128, 256, 1, 260, 97, 97, False, True),
+    (128, 256, 3, 100, 257, 257, False, False),
+    (128, 256, 1, 200, 300, 700, False, False),
 ], ids=lambda v: str(v))
 def test_prefill_many_items_per_workgroup(d, dv, B, H, nq, nk, causal, pre_norm):
     w = _custom(B, H, nq, nk, d, dv, "bf16", causal, seed=B * 1000 + H + nq)

@@ -27,7 +27,7 @@ import torch
 __all__ = [
     "fwd", "fwd_fp8", "fwd_train", "qkv_proj", "bwd", "bwd_workspace_size", "diag", "decode",
     "decode_workspace_size", "decode_default_splits", "abi_version", "library_path",
-    "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
+    "prefill_kernel_name", "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,14 @@ _lib = None
 
 def library_path() -> str:
     return _LIB_PATH
+
+
+def prefill_kernel_name(d: int, dv: int, dtype: str = "bf16") -> str:
+    """Name of the kernel diffattn_fwd launches for these sizes (as a profiler
+    lists it), so measurements can be matched to kernels."""
+    if dtype == "f32":
+        return "prefill_f32_kernel"
+    return "prefill_bf16_twopass_kernel" if (d, dv) == (128, 256) else "prefill_bf16_kernel"
 
 
 def lib():

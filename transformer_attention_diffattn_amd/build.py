@@ -19,12 +19,16 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libdiffattn.so")
-SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_bf16_wide.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "diag.hip", "proj.hip"]
+# the roofline microbenchmarks: a library of their own, not part of the operator
+PEAKS_SRC = "peaks.hip"
+PEAKS_LIB = os.path.join(LIBDIR, "libdiffattn_peaks.so")
+SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_twopass.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "diag.hip", "proj.hip"]
 # Per-source extra flags.  The narrow-head prefill kernel keeps its score
 # accumulators in ordinary VGPRs, where the softmax reads them without a copy
 # out of the accumulation registers; the compiler's default heuristic would
 # put every matrix accumulator in AGPRs.
-EXTRA_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "prefill_twopass.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,14 +54,19 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         if len(procs) >= jobs:
             _wait(procs.pop(0))
+    peaks_obj = os.path.join(BUILD, os.path.splitext(PEAKS_SRC)[0] + ".o")
+    procs.append((PEAKS_SRC, subprocess.Popen(
+        [HIPCC, *FLAGS, "-c", os.path.join(CSRC, PEAKS_SRC), "-o", peaks_obj],
+        stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     for p in procs:
         _wait(p)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (PEAKS_LIB, [peaks_obj])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -115,8 +115,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
 hipError_t launch_prefill_fp8qk(const PrefillArgs& a, int d, int dv, bool causal,
                                 hipStream_t stream);
 hipError_t launch_qkv_proj_bf16(const ProjArgs& a, hipStream_t stream);
-hipError_t launch_prefill_bf16_wide(const PrefillArgs& a, int d, int dv, bool causal,
-                                    hipStream_t stream);
+// head_dim 128, v_dim 256: the two-sweep kernel (also the training forward)
+hipError_t launch_prefill_bf16_twopass(const PrefillArgs& a, int d, int dv, bool causal,
+                                       hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);

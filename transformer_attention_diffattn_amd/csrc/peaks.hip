@@ -1,0 +1,139 @@
+// Roofline microbenchmarks for gfx950: the rates the operator's kernels are
+// measured against, next to the published figures.
+//
+//   peaks_mfma_bf16   dense bf16 matrix rate: every wave issues independent
+//                     v_mfma_f32_32x32x16_bf16 chains (32768 flops each);
+//   peaks_read_bw     streaming HBM reads: 16-byte loads over a buffer much
+//                     larger than the caches, each byte read once;
+//   peaks_exp_rate    v_exp_f32 throughput (the softmax's transcendental),
+//                     independent chains in every lane; and the same for
+//                     v_fma_f32, so the two can be compared.
+//
+// Each entry point launches on the given stream and returns a hipError_t
+// code; the caller times the launch with events and divides the work it
+// reports.  The kernels write one value per thread only when an impossible
+// condition holds, so the work cannot be optimised away and nothing is
+// written in practice.  Built into a library of its own: these are
+// measurement tools, not part of the operator's interface.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChains = 4;  // independent accumulators per wave
+
+__global__ __launch_bounds__(256) void mfma_bf16_kernel(float* sink, int iters) {
+    const int t = threadIdx.x;
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (float)((t + i) & 7));
+        b[i] = (__bf16)(0.002f * (float)((t * 3 + i) & 7));
+    }
+    f32x16 c[kChains];
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) c[k] = f32x16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < kChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) s += c[k][0] + c[k][15];
+    if (s == -1.2345f) sink[blockIdx.x * blockDim.x + t] = s;
+}
+
+__global__ __launch_bounds__(512) void read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                   uint32_t* sink) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    // four loads in flight per lane
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 x0 = __builtin_nontemporal_load(src + i);
+        const u32x4 x1 = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 x2 = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 x3 = __builtin_nontemporal_load(src + i + 3 * stride);
+        acc ^= (x0[0] ^ x0[1] ^ x0[2] ^ x0[3]) + (x1[0] ^ x1[1] ^ x1[2] ^ x1[3]) +
+               (x2[0] ^ x2[1] ^ x2[2] ^ x2[3]) + (x3[0] ^ x3[1] ^ x3[2] ^ x3[3]);
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 x = src[i];
+        acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+    }
+    if (acc == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+constexpr int kExpChains = 8;
+
+// x <- 2^-x keeps every chain in [0.5, 1]: the negation is a source modifier
+// of the one instruction per step
+__global__ __launch_bounds__(256) void exp_kernel(float* sink, int iters) {
+    float x[kExpChains];
+#pragma unroll
+    for (int k = 0; k < kExpChains; ++k) x[k] = 0.1f * (float)k + 1e-3f * (float)(threadIdx.x & 63);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < kExpChains; ++k) x[k] = __builtin_amdgcn_exp2f(-x[k]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kExpChains; ++k) s += x[k];
+    if (s == -1.2345f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// x <- x * c + d with |c| < 1: one v_fma_f32 per step and chain
+__global__ __launch_bounds__(256) void fma_kernel(float* sink, int iters, float c, float d) {
+    float x[kExpChains];
+#pragma unroll
+    for (int k = 0; k < kExpChains; ++k) x[k] = 0.1f * (float)k + 1e-3f * (float)(threadIdx.x & 63);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < kExpChains; ++k) x[k] = fmaf(x[k], c, d);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kExpChains; ++k) s += x[k];
+    if (s == -1.2345f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Flops of one peaks_mfma_bf16 launch: blocks * 4 waves * iters * kChains * 32768.
+// sink: blocks * 256 floats of device memory (never written in practice).
+int peaks_mfma_bf16(void* sink, int blocks, int iters, void* stream) {
+    hipLaunchKernelGGL(mfma_bf16_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (float*)sink, iters);
+    return (int)hipGetLastError();
+}
+
+// Reads n16 16-byte chunks of src once. sink: blocks * 512 uint32 of device memory.
+int peaks_read_bw(const void* src, int64_t n16, void* sink, int blocks, void* stream) {
+    hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                       (const u32x4*)src, n16, (uint32_t*)sink);
+    return (int)hipGetLastError();
+}
+
+// exp2 (fma when use_fma) instructions of one launch: blocks * 256 * iters * 8.
+// sink: blocks * 256 floats of device memory.
+int peaks_vector_rate(void* sink, int blocks, int iters, int use_fma, void* stream) {
+    if (use_fma)
+        hipLaunchKernelGGL(fma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                           (float*)sink, iters, 0.5f, 0.25f);
+    else
+        hipLaunchKernelGGL(exp_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                           (float*)sink, iters);
+    return (int)hipGetLastError();
+}
+
+int peaks_mfma_chains(void) { return kChains; }
+int peaks_vector_chains(void) { return kExpChains; }
+
+}  // extern "C"

@@ -1,6 +1,6 @@
 // Fused Differential Attention prefill for bf16 inputs on gfx950 (CDNA4):
 // the kernels for head_dim 32 and 64, the training forward, and the variant
-// with e4m3 queries and keys.  The kernel body is prefill_items in
+// with e4m3 queries and keys (head_dim 128 is in prefill_twopass.hip).  The kernel body is prefill_items in
 // prefill_core.h; this file is compiled with the MFMA accumulators in
 // ordinary VGPRs, where the softmax reads the scores without a copy.
 
@@ -63,7 +63,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
                                hipStream_t stream) {
     if (d == 32 && dv == 64) return launch_dims<32, 64, false>(a, causal, stream);
     if (d == 64 && dv == 128) return launch_dims<64, 128, false>(a, causal, stream);
-    if (d == 128 && dv == 256) return launch_prefill_bf16_wide(a, d, dv, causal, stream);
+    if (d == 128 && dv == 256) return launch_prefill_bf16_twopass(a, d, dv, causal, stream);
     return hipErrorInvalidValue;
 }
 

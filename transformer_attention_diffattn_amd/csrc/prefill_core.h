@@ -1,7 +1,7 @@
 // The bf16 prefill forward for head_dim 32 and 64 as a template
 // (prefill_items), kept apart from its instantiations in prefill_bf16.hip
 // (the forward, the training forward, the e4m3-score variant).  head_dim 128
-// is in prefill_bf16_wide.hip.
+// is in prefill_twopass.hip.
 //
 // Fused Differential Attention prefill for bf16 inputs on gfx950 (CDNA4).
 //
