@@ -14,9 +14,10 @@
 // Work decomposition
 //   A work item is 128 query rows of one (batch, head), taken by one
 //   workgroup of 8 wavefronts.  The grid is persistent (one workgroup per
-//   compute unit when there are more items than units): items are sorted
-//   longest-first and dealt out in a snake, so the causal lengths even out
-//   and no workgroup launches per item.  Wave
+//   compute unit when there are more items than units): items are dealt out
+//   longest-first in a snake, so the causal lengths even out and no
+//   workgroup launches per item, and head by head within each XCD, so the
+//   XCD's workgroups sweep one head's K and V together (schedule.h).  Wave
 //   w owns query block w % 4 (32 rows) of map w / 4: the two softmax maps of
 //   a row are computed by two waves, and the lambda-weighted subtraction is
 //   done once, through LDS, in the epilogue.  Splitting by map halves the
@@ -91,6 +92,7 @@
 #pragma once
 
 #include "internal.h"
+#include "schedule.h"
 
 #include <math.h>
 
@@ -272,22 +274,15 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::kSmemElems];
 
 
-    // Work items (query tile, batch*head), longest causal tiles first: item k
-    // takes query tile t = k / BH (counted from the last one) of head k % BH.
-    // The grid is persistent: in round r workgroup w takes item r G + w for
-    // even r and r G + w' for odd r, a snake over the sorted items that evens
-    // out the causal lengths.  Workgroups are dealt to the 8 XCDs round-robin,
-    // so w' reverses w's slot within its XCD (w' = w mod 8 + 8 (G/8 - 1 -
-    // w/8)): every item of a head then runs on one XCD and its K/V on one L2.
+    // Work items (query tile, batch*head), taken by the persistent grid in the
+    // order of prefill_item (schedule.h): head-major per XCD, longest causal
+    // tiles first, in a snake.
     const int BH = a.B * a.H;
     const int nqt = (a.Nq + C::kBr - 1) / C::kBr;
-    const int n_items = nqt * BH;
     const int G = gridDim.x;
-    const int w_even = blockIdx.x;
-    const int w_odd = (G & 7) == 0 ? (w_even & 7) + 8 * (G / 8 - 1 - w_even / 8) : G - 1 - w_even;
     for (int r = 0;; ++r) {
-    const int k_item = r * G + ((r & 1) ? w_odd : w_even);
-    if (k_item >= n_items) break;
+    int t, bh;
+    if (!prefill_item(r, blockIdx.x, G, nqt, BH, t, bh)) break;
     // opaque per item, so that nothing derived from the lane is hoisted out of
     // the item loop and held live across it
     int tid = threadIdx.x;
@@ -298,8 +293,6 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     const int lh = lane >> 5;
     const int qb = wave & (kBlocks - 1);  // query block
     const int map = wave >> 2;            // 0: first softmax map, 1: the lambda map
-    const int t = k_item / BH;
-    const int bh = k_item - t * BH;
     const int qt = CAUSAL ? (nqt - 1 - t) : t;
     const int h = bh % a.H;
     const float lam_h = a.lam[h];

@@ -28,8 +28,8 @@
 // Work decomposition
 //   A work item is 128 query rows of one (batch, head), taken by one
 //   workgroup of 8 wavefronts; the grid is persistent and deals items out
-//   longest-first in a snake, all items of a head on one XCD (as in the
-//   narrow-head kernel).  Wave w owns query block w % 4 (32 rows) and map
+//   head by head within each XCD, longest-first in a snake (schedule.h): the
+//   XCD's workgroups sweep one head's K and V together, through its L2.  Wave w owns query block w % 4 (32 rows) and map
 //   w / 4: it computes that map's scores and statistics, and in sweep 2 the
 //   P.V of half of the dv channels (map 1's wave channels 0..127, map 2's
 //   wave 128..255).  Both waves of a query block need the full P, so each
@@ -65,6 +65,7 @@
 // 16-byte chunk so that the operand reads hit distinct banks.
 
 #include "internal.h"
+#include "schedule.h"
 
 #include <math.h>
 
@@ -177,15 +178,10 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
 
     const int BH = a.B * a.H;
     const int nqt = (a.Nq + kBr - 1) / kBr;
-    const int n_items = nqt * BH;
     const int G = gridDim.x;
-    // the narrow-head kernel's snake: round r takes item r G + w (even r) or
-    // r G + w' (odd r), w' reversing w's slot within its XCD
-    const int w_even = blockIdx.x;
-    const int w_odd = (G & 7) == 0 ? (w_even & 7) + 8 * (G / 8 - 1 - w_even / 8) : G - 1 - w_even;
     for (int r = 0;; ++r) {
-    const int k_item = r * G + ((r & 1) ? w_odd : w_even);
-    if (k_item >= n_items) break;
+    int t, bh;
+    if (!prefill_item(r, blockIdx.x, G, nqt, BH, t, bh)) break;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int wave = tid >> 6;
@@ -194,8 +190,6 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
     const int lh = lane >> 5;
     const int qb = wave & (kBlocks - 1);
     const int map = wave >> 2;  // 0: first softmax map, 1: the lambda map
-    const int t = k_item / BH;
-    const int bh = k_item - t * BH;
     const int qt = CAUSAL ? (nqt - 1 - t) : t;
     const int h = bh % a.H;
     const float lam_h = a.lam[h];
