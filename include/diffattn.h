@@ -233,6 +233,27 @@ int diffattn_decode(const void* q1, const void* q2, const void* k1_cache,
                     int32_t num_splits, const diffattn_dims* dims, void* stream);
 
 /*
+ * Decode that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, results and errors as
+ * diffattn_decode, without workspace and workspace_bytes: with more than one
+ * split the partial results go to a scratch array the library holds in
+ * device memory, DIFFATTN_NOALLOC_SCRATCH_BYTES per GPU, kept until the
+ * process ends.  A call whose partials would not fit returns
+ * DIFFATTN_ERR_WORKSPACE and launches nothing (ask for fewer splits).  All
+ * calls on one GPU share that array, so calls that overlap in time on one
+ * GPU (different streams, or threads) race; calls on one stream are
+ * ordered.  Nothing in the array needs to start at zero: every record a call
+ * reads it has written first.  Calls no allocating routine.
+ */
+#define DIFFATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int diffattn_decode_noalloc(const void* q1, const void* q2, const void* k1_cache,
+                            const void* k2_cache, const void* v_cache, int32_t kv_capacity,
+                            const int32_t* kv_lens, const float* lambda, float lambda_init,
+                            void* out, int32_t num_splits, const diffattn_dims* dims,
+                            void* stream);
+
+/*
  * The split count diffattn_decode uses for num_splits = 0 on the current
  * device (queries the device's compute-unit count once).  Returns a value
  * >= 1, or 0 if dims is invalid or the device cannot be queried.

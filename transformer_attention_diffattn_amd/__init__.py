@@ -26,6 +26,7 @@ import torch
 
 __all__ = [
     "fwd", "fwd_fp8", "fwd_train", "qkv_proj", "bwd", "bwd_workspace_size", "diag", "decode",
+    "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "decode_workspace_size", "decode_default_splits", "abi_version", "library_path",
     "prefill_kernel_name", "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
 ]
@@ -38,6 +39,7 @@ SUPPORTED_DIMS = ((32, 64), (64, 128), (128, 256))
 F32, BF16 = 0, 1
 FLAG_PRE_NORM = 1
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 16 << 20  # DIFFATTN_NOALLOC_SCRATCH_BYTES
 
 
 class DiffAttnError(RuntimeError):
@@ -89,6 +91,9 @@ def lib():
         L.diffattn_decode.restype = I
         L.diffattn_decode.argtypes = [P, P, P, P, P, ctypes.c_int32, P, P, F, P, P,
                                       ctypes.c_size_t, ctypes.c_int32, DP, P]
+        L.diffattn_decode_noalloc.restype = I
+        L.diffattn_decode_noalloc.argtypes = [P, P, P, P, P, ctypes.c_int32, P, P, F, P,
+                                              ctypes.c_int32, DP, P]
         L.diffattn_decode_default_splits.restype = ctypes.c_int32
         L.diffattn_decode_default_splits.argtypes = [DP]
         L.diffattn_decode_workspace_size.restype = ctypes.c_size_t
@@ -387,14 +392,7 @@ def decode_workspace_size(B: int, H: int, L: int, d: int, dv: int, num_splits: i
         ctypes.byref(_decode_dims(B, H, L, d, dv, BF16, 1e-5, False)), int(num_splits)))
 
 
-def decode(q1: torch.Tensor, q2: torch.Tensor, k1_cache: torch.Tensor, k2_cache: torch.Tensor,
-           v_cache: torch.Tensor, lam, lambda_init: float = 0.8, kv_len: Optional[int] = None,
-           kv_lens: Optional[torch.Tensor] = None, num_splits: int = 0, eps: float = 1e-5,
-           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-           pre_norm: bool = False) -> torch.Tensor:
-    """KV-cache decode.  q1, q2 [B,H,d]; caches [B,H,cap,d] / [B,H,cap,dv].
-    kv_len: cache length used (default: cap); kv_lens: optional int32 [B] of
-    per-sequence lengths (clamped to [0, kv_len]).  Returns out [B,H,dv]."""
+def _decode_prep(q1, q2, k1_cache, k2_cache, v_cache, lam, kv_len, kv_lens, eps, out, pre_norm):
     ts = (q1, q2, k1_cache, k2_cache, v_cache)
     _require(all(t.is_cuda for t in ts), "inputs must be GPU tensors")
     _require(all(t.device == q1.device for t in ts), "inputs must share one device")
@@ -417,6 +415,19 @@ def decode(q1: torch.Tensor, q2: torch.Tensor, k1_cache: torch.Tensor, k2_cache:
              "out must be a contiguous [B,H,dv] tensor")
     lam_t = _lam_tensor(lam, H, q1.device)
     dims = _decode_dims(B, H, L, d, dv, _dtype_code(q1), eps, pre_norm)
+    return cap, out, lam_t, dims
+
+
+def decode(q1: torch.Tensor, q2: torch.Tensor, k1_cache: torch.Tensor, k2_cache: torch.Tensor,
+           v_cache: torch.Tensor, lam, lambda_init: float = 0.8, kv_len: Optional[int] = None,
+           kv_lens: Optional[torch.Tensor] = None, num_splits: int = 0, eps: float = 1e-5,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           pre_norm: bool = False) -> torch.Tensor:
+    """KV-cache decode.  q1, q2 [B,H,d]; caches [B,H,cap,d] / [B,H,cap,dv].
+    kv_len: cache length used (default: cap); kv_lens: optional int32 [B] of
+    per-sequence lengths (clamped to [0, kv_len]).  Returns out [B,H,dv]."""
+    cap, out, lam_t, dims = _decode_prep(q1, q2, k1_cache, k2_cache, v_cache, lam, kv_len,
+                                         kv_lens, eps, out, pre_norm)
     need = int(lib().diffattn_decode_workspace_size(ctypes.byref(dims), int(num_splits)))
     ws_ptr, ws_bytes = None, 0
     if need > 0:
@@ -429,5 +440,26 @@ def decode(q1: torch.Tensor, q2: torch.Tensor, k1_cache: torch.Tensor, k2_cache:
                                lam_t.data_ptr(), float(lambda_init), out.data_ptr(), ws_ptr,
                                ws_bytes, int(num_splits), ctypes.byref(dims),
                                _stream_ptr(q1.device))
+    _check(st)
+    return out
+
+
+def decode_noalloc(q1: torch.Tensor, q2: torch.Tensor, k1_cache: torch.Tensor,
+                   k2_cache: torch.Tensor, v_cache: torch.Tensor, lam, lambda_init: float = 0.8,
+                   kv_len: Optional[int] = None, kv_lens: Optional[torch.Tensor] = None,
+                   num_splits: int = 0, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                   pre_norm: bool = False) -> torch.Tensor:
+    """As decode, through diffattn_decode_noalloc: no workspace; the library's
+    fixed scratch array (NOALLOC_SCRATCH_BYTES per GPU) holds the split-K
+    partials.  Pass `out` (and a device lambda) for a call that allocates
+    nothing at all."""
+    cap, out, lam_t, dims = _decode_prep(q1, q2, k1_cache, k2_cache, v_cache, lam, kv_len,
+                                         kv_lens, eps, out, pre_norm)
+    st = lib().diffattn_decode_noalloc(q1.data_ptr(), q2.data_ptr(), k1_cache.data_ptr(),
+                                       k2_cache.data_ptr(), v_cache.data_ptr(), cap,
+                                       kv_lens.data_ptr() if kv_lens is not None else None,
+                                       lam_t.data_ptr(), float(lambda_init), out.data_ptr(),
+                                       int(num_splits), ctypes.byref(dims),
+                                       _stream_ptr(q1.device))
     _check(st)
     return out

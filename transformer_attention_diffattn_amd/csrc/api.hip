@@ -100,6 +100,67 @@ int32_t resolve_splits(const diffattn_dims* dm, int32_t num_splits) {
 
 using namespace diffattn;
 
+namespace {
+
+// diffattn_decode and diffattn_decode_noalloc: noalloc takes the partials'
+// memory from the library's scratch array instead of `workspace`.
+int decode_common(const void* q1, const void* q2, const void* k1_cache, const void* k2_cache,
+                  const void* v_cache, int32_t kv_capacity, const int32_t* kv_lens,
+                  const float* lambda, float lambda_init, void* out, void* workspace,
+                  size_t workspace_bytes, bool noalloc, int32_t num_splits,
+                  const diffattn_dims* dims, void* stream) {
+    using namespace diffattn;
+    int st = check_decode_dims(dims);
+    if (st != DIFFATTN_OK) return st;
+    const void* ptrs[] = {q1, q2, k1_cache, k2_cache, v_cache, lambda, out};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return DIFFATTN_ERR_INVALID;
+    if (kv_lens && ((uintptr_t)kv_lens & 3u)) return DIFFATTN_ERR_INVALID;
+    if (!isfinite(lambda_init) || num_splits < 0) return DIFFATTN_ERR_INVALID;
+    if (kv_capacity < dims->seq_k) return DIFFATTN_ERR_INVALID;
+
+    const int32_t splits = resolve_splits(dims, num_splits);
+    if (splits < 1) return DIFFATTN_ERR_HIP;  // device query failed
+    if (splits > 1) {
+        const size_t need = (size_t)dims->batch * dims->heads * splits *
+                            decode_record_floats(dims->v_dim) * sizeof(float);
+        if (noalloc) {
+            if (need > DIFFATTN_NOALLOC_SCRATCH_BYTES) return DIFFATTN_ERR_WORKSPACE;
+            size_t have = 0;
+            if (decode_scratch(&workspace, &have) != hipSuccess) return DIFFATTN_ERR_HIP;
+            if (need > have) return DIFFATTN_ERR_WORKSPACE;
+        } else if (!workspace || !aligned16(workspace) || workspace_bytes < need) {
+            return DIFFATTN_ERR_WORKSPACE;
+        }
+    }
+
+    DecodeArgs a;
+    a.q1 = q1;
+    a.q2 = q2;
+    a.k1 = k1_cache;
+    a.k2 = k2_cache;
+    a.v = v_cache;
+    a.kv_lens = kv_lens;
+    a.lam = lambda;
+    a.out = out;
+    a.partials = (float*)workspace;
+    a.B = dims->batch;
+    a.H = dims->heads;
+    a.L = dims->seq_k;
+    a.cap = kv_capacity;
+    a.splits = splits;
+    a.chunk = split_chunk(dims->seq_k, splits);
+    a.lambda_init = lambda_init;
+    a.eps = dims->eps;
+    a.scale_log2 = scale_log2(dims->head_dim);
+    a.flags = dims->flags;
+    const hipError_t e = launch_decode(a, dims->head_dim, dims->v_dim,
+                                       dims->dtype == DIFFATTN_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 int diffattn_abi_version(void) { return DIFFATTN_ABI_VERSION; }
@@ -381,47 +442,18 @@ int diffattn_decode(const void* q1, const void* q2, const void* k1_cache, const 
                     const float* lambda, float lambda_init, void* out, void* workspace,
                     size_t workspace_bytes, int32_t num_splits, const diffattn_dims* dims,
                     void* stream) {
-    int st = check_decode_dims(dims);
-    if (st != DIFFATTN_OK) return st;
-    const void* ptrs[] = {q1, q2, k1_cache, k2_cache, v_cache, lambda, out};
-    for (const void* p : ptrs)
-        if (!p || !aligned16(p)) return DIFFATTN_ERR_INVALID;
-    if (kv_lens && ((uintptr_t)kv_lens & 3u)) return DIFFATTN_ERR_INVALID;
-    if (!isfinite(lambda_init) || num_splits < 0) return DIFFATTN_ERR_INVALID;
-    if (kv_capacity < dims->seq_k) return DIFFATTN_ERR_INVALID;
+    return decode_common(q1, q2, k1_cache, k2_cache, v_cache, kv_capacity, kv_lens, lambda,
+                         lambda_init, out, workspace, workspace_bytes, false, num_splits, dims,
+                         stream);
+}
 
-    const int32_t splits = resolve_splits(dims, num_splits);
-    if (splits < 1) return DIFFATTN_ERR_HIP;  // device query failed
-    if (splits > 1) {
-        const size_t need = (size_t)dims->batch * dims->heads * splits *
-                            decode_record_floats(dims->v_dim) * sizeof(float);
-        if (!workspace || !aligned16(workspace) || workspace_bytes < need)
-            return DIFFATTN_ERR_WORKSPACE;
-    }
-
-    DecodeArgs a;
-    a.q1 = q1;
-    a.q2 = q2;
-    a.k1 = k1_cache;
-    a.k2 = k2_cache;
-    a.v = v_cache;
-    a.kv_lens = kv_lens;
-    a.lam = lambda;
-    a.out = out;
-    a.partials = (float*)workspace;
-    a.B = dims->batch;
-    a.H = dims->heads;
-    a.L = dims->seq_k;
-    a.cap = kv_capacity;
-    a.splits = splits;
-    a.chunk = split_chunk(dims->seq_k, splits);
-    a.lambda_init = lambda_init;
-    a.eps = dims->eps;
-    a.scale_log2 = scale_log2(dims->head_dim);
-    a.flags = dims->flags;
-    const hipError_t e = launch_decode(a, dims->head_dim, dims->v_dim,
-                                       dims->dtype == DIFFATTN_BF16, (hipStream_t)stream);
-    return e == hipSuccess ? DIFFATTN_OK : DIFFATTN_ERR_HIP;
+int diffattn_decode_noalloc(const void* q1, const void* q2, const void* k1_cache,
+                            const void* k2_cache, const void* v_cache, int32_t kv_capacity,
+                            const int32_t* kv_lens, const float* lambda, float lambda_init,
+                            void* out, int32_t num_splits, const diffattn_dims* dims,
+                            void* stream) {
+    return decode_common(q1, q2, k1_cache, k2_cache, v_cache, kv_capacity, kv_lens, lambda,
+                         lambda_init, out, nullptr, 0, true, num_splits, dims, stream);
 }
 
 }  // extern "C"

@@ -26,7 +26,10 @@
 //   3. updates both online softmaxes (wave max, exp2, lane-partial sums);
 //   4. accumulates p1 * V and p2 * V into per-lane channel accumulators.
 
+#include "../../include/diffattn.h"
 #include "internal.h"
+
+#include <mutex>
 
 #include <math.h>
 
@@ -415,6 +418,32 @@ hipError_t launch_t(const DecodeArgs& a, int d, int dv, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Partial records of diffattn_decode_noalloc: a fixed device array instead of
+// a caller workspace.  Host code must not pass the array's name to a kernel
+// (on the host it is a stand-in, not a device address): decode_scratch looks
+// up each device's own copy once, with that device current, and the kernels
+// get that address.
+static __device__ __align__(256) uint8_t scratch[DIFFATTN_NOALLOC_SCRATCH_BYTES];
+
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream) {
     return bf16 ? launch_t<uint16_t>(a, d, dv, stream) : launch_t<float>(a, d, dv, stream);

@@ -121,6 +121,9 @@ hipError_t launch_prefill_bf16_twopass(const PrefillArgs& a, int d, int dv, bool
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);
+// Device address and size of the current device's decode scratch array (the
+// partials of diffattn_decode_noalloc), looked up once per device.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 hipError_t launch_backward_bf16(const BackwardArgs& a, int d, int dv, bool causal,
                                 hipStream_t stream);
 hipError_t launch_diag_bf16(const DiagArgs& a, int d, bool causal, hipStream_t stream);
