@@ -33,9 +33,10 @@
 //   w / 4: it computes that map's scores and statistics, and in sweep 2 the
 //   P.V of half of the dv channels (map 1's wave channels 0..127, map 2's
 //   wave 128..255).  Both waves of a query block need the full P, so each
-//   writes its map's weights, scaled by 2^15 and rounded toward zero to fp16,
-//   to LDS; after the tile's barrier both read both and form
-//   P = x1 - x2 in fp16 arithmetic, then round P to bf16 for the product.
+//   writes its map's weights, scaled by 2^15 and rounded toward zero to fp16
+//   (the lambda map's negated), to LDS and keeps them; after the tile's
+//   barrier each reads the other's and forms P = x1 - x2 in fp16 arithmetic,
+//   then rounds P to bf16 for the product.
 //   The two waves compute bit-identical P, so the two halves of a row agree.
 //   The weights are at most 1 (times 2^15 < 65504), fp16 keeps 11 bits where
 //   bf16 keeps 8, and the difference is rounded relative to itself: the
@@ -146,16 +147,19 @@ __device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, int64_t bytes) {
 // __builtin_bit_cast reads element 0 whatever i is.
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
-// P = x1 - x2 for the 8 weight pairs of a tile (two 16-byte exchange reads
-// each), rounded to bf16 in B-operand order (registers 8kb .. 8kb+7)
-__device__ __forceinline__ void combine(const u32x4 (&x1)[2], const u32x4 (&x2)[2], bf16x8 (&pb)[2]) {
+// P = x1 - x2 for the 8 weight pairs of a tile as own + partner: the first
+// map's wave stores x1, the lambda map's wave -x2, each keeps its own values
+// and reads the other's (two 16-byte reads); fp16 addition commutes, so both
+// waves get the same bits.  Rounded to bf16 in B-operand order (registers
+// 8kb .. 8kb+7).
+__device__ __forceinline__ void combine(const u32x4 (&own)[2], const u32x4 (&other)[2], bf16x8 (&pb)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 v1 = x1[kb], v2 = x2[kb];
+        const u32x4 v1 = own[kb], v2 = other[kb];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t w1 = v1[c], w2 = v2[c];
-            const f16x2 d = as_f16x2(w1) - as_f16x2(w2);
+            const f16x2 d = as_f16x2(w1) + as_f16x2(w2);
             pb[kb][2 * c] = (__bf16)(float)d[0];
             pb[kb][2 * c + 1] = (__bf16)(float)d[1];
         }
@@ -412,11 +416,13 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
     const float alam = fabsf(lam_h);
     int e_sc = 0;
     if (alam > 1.f) (void)frexpf(alam, &e_sc);
-    const float lc = map ? __builtin_amdgcn_logf(alam) : 0.f;  // log2: 0 for c = 1
+    const bool lambda_map = __builtin_amdgcn_readfirstlane(map) != 0;
+    const float lc = lambda_map ? __builtin_amdgcn_logf(alam) : 0.f;  // log2: 0 for c = 1
     const float base2 = ((m + __builtin_amdgcn_logf(L)) - (float)(kXScale - e_sc)) - lc;
-    // the lambda map's wave stores x2 = fp16(2^(15-e) lambda a_2) with the
-    // sign of lambda (its exponentials give |lambda| a_2), so P = x1 - x2
-    const bool flip = map && lam_h < 0.f;
+    // the lambda map's wave stores -x2 = -fp16(2^(15-e) lambda a_2): its
+    // exponentials give |lambda| a_2, negated unless lambda < 0
+    const bool flip = lambda_map && !(lam_h < 0.f);
+    u32x4 own[2];  // this wave's stored weights of the previous tile
 
     // ---- sweep 2.  Iteration g (tile j = g - nkt): P of tile j-1 from the
     // exchange slot and its P.V (MFMA), scores of entry g+1 (MFMA), weights
@@ -427,18 +433,16 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
         constexpr bool NEXT = decltype(next)::value;
         const int gg = nkt + j;
         bf16x8 pb[2];
-        u32x4 x1[2], x2[2];
+        u32x4 other[2];
         if constexpr (PREV) {
             const int slot = (gg - 1) & 1;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                x1[i] = *(const u32x4*)(xchg_at(slot, qb) + 1024 * i + 16 * lane);
-                x2[i] = *(const u32x4*)(xchg_at(slot, 4 + qb) + 1024 * i + 16 * lane);
-            }
+            for (int i = 0; i < 2; ++i)
+                other[i] = *(const u32x4*)(xchg_at(slot, wave ^ 4) + 1024 * i + 16 * lane);
         }
         if constexpr (NEXT) scores((gg + 1) & (kStages - 1), nxt);
         if constexpr (PREV) {
-            combine(x1, x2, pb);
+            combine(own, other, pb);
             const int vst = (gg - 1) & (kStages - 1);
 #pragma unroll
             for (int db = 0; db < kNDB; ++db) {
@@ -460,10 +464,12 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) xw[i] ^= 0x80008000u;
         }
+        own[0] = u32x4{xw[0], xw[1], xw[2], xw[3]};
+        own[1] = u32x4{xw[4], xw[5], xw[6], xw[7]};
         {
             uint8_t* dst = xchg_at(gg & 1, wave) + 16 * lane;
-            *(u32x4*)dst = u32x4{xw[0], xw[1], xw[2], xw[3]};
-            *(u32x4*)(dst + 1024) = u32x4{xw[4], xw[5], xw[6], xw[7]};
+            *(u32x4*)dst = own[0];
+            *(u32x4*)(dst + 1024) = own[1];
         }
         issue_v(j + 2);
         issue_k(gg + 4);
@@ -498,13 +504,11 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
         const int gg = 2 * nkt;
         const int slot = (gg - 1) & 1;
         bf16x8 pb[2];
-        u32x4 y1[2], y2[2];
+        u32x4 other[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            y1[i] = *(const u32x4*)(xchg_at(slot, qb) + 1024 * i + 16 * lane);
-            y2[i] = *(const u32x4*)(xchg_at(slot, 4 + qb) + 1024 * i + 16 * lane);
-        }
-        combine(y1, y2, pb);
+        for (int i = 0; i < 2; ++i)
+            other[i] = *(const u32x4*)(xchg_at(slot, wave ^ 4) + 1024 * i + 16 * lane);
+        combine(own, other, pb);
         const int vst = (gg - 1) & (kStages - 1);
 #pragma unroll
         for (int db = 0; db < kNDB; ++db) {
