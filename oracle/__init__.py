@@ -33,15 +33,28 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "diffattn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
 _lib = None
 
 
-def build(force: bool = True, src: str = _SRC, lib: str = _LIB) -> str:
-    """Compile the oracle with gcc (-O2, IEEE semantics kept: no fast-math)."""
+def build(force: bool = True, src: str = _SRC, lib: str = _LIB, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, IEEE semantics kept: no fast-math).
+
+    sanitize: build liboracle_san.so with clang's AddressSanitizer and
+    UndefinedBehaviorSanitizer instead (the ROCm LLVM's clang, whose ASan
+    runtime a process must preload to load it)."""
+    if sanitize and lib == _LIB:
+        lib = _SAN_LIB
     if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(src):
         tmp = lib + ".tmp"
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-               "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+        if sanitize:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+                   "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                   "-shared-libsan", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+                   "-Wextra", "-o", tmp, src, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                   "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, lib)
     return lib
@@ -99,8 +112,12 @@ class Oracle:
 def _load() -> Oracle:
     global _lib
     if _lib is None:
-        build(force=False)
-        _lib = Oracle(_LIB)
+        # DIFFATTN_ORACLE_LIB: another build of the same source (the sanitized one)
+        path = os.environ.get("DIFFATTN_ORACLE_LIB")
+        if not path:
+            build(force=False)
+            path = _LIB
+        _lib = Oracle(path)
     return _lib
 
 

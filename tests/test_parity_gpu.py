@@ -216,18 +216,25 @@ def test_causal_row0_closed_form():
     assert_close(out[0, :, 0], ref.cpu().numpy(), torch.bfloat16, "row 0")
 
 
-def test_deterministic_and_canary():
-    w = _custom(2, 4, 333, 333, 64, 128, "bf16", True, seed=31)
+# Bitwise repeatability and no stray writes: the output sits between two
+# guard bands of a larger buffer; 100 launches must give identical bits and
+# leave both bands untouched.
+@pytest.mark.parametrize("dims", da.SUPPORTED_DIMS, ids=lambda t: f"d{t[0]}")
+def test_deterministic_and_canary(dims):
+    d, dv = dims
+    w = _custom(2, 4, 333, 333, d, dv, "bf16", True, seed=31)
     x = _to(workloads.make_prefill(w, device="cpu"))
-    n = 2 * 4 * 333 * 128
-    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
-    out = buf[:n].view(2, 4, 333, 128)
+    n = 2 * 4 * 333 * dv
+    guard = 4096
+    buf = torch.full((guard + n + guard,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[guard:guard + n].view(2, 4, 333, dv)
     da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=True, out=out)
     first = out.clone()
-    for _ in range(3):
+    for _ in range(100):
         da.fwd(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], causal=True, out=out)
         assert torch.equal(out, first)
-    assert bool((buf[n:] == 7.0).all())
+    assert bool((buf[:guard] == 7.0).all()), "write before the output"
+    assert bool((buf[guard + n:] == 7.0).all()), "write past the output"
 
 
 # --------------------------------------------------------------------------

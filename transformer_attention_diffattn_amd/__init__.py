@@ -32,7 +32,8 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "_lib", "libdiffattn.so")
+# DIFFATTN_LIBRARY: another build of the same library (the host-sanitized one)
+_LIB_PATH = os.environ.get("DIFFATTN_LIBRARY") or os.path.join(_HERE, "_lib", "libdiffattn.so")
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "diffattn.h")
 
 SUPPORTED_DIMS = ((32, 64), (64, 128), (128, 256))
