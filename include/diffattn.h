@@ -84,6 +84,8 @@ int diffattn_abi_version(void);
 
 /* A static, human-readable name for a status code. */
 const char* diffattn_status_string(int status);
+/* The same function under a shorter name. */
+const char* diffattn_status_str(int status);
 
 /*
  * Prefill (fused forward over all query rows).

@@ -176,6 +176,8 @@ const char* diffattn_status_string(int status) {
     }
 }
 
+const char* diffattn_status_str(int status) { return diffattn_status_string(status); }
+
 int diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2, const void* v,
                  const float* lambda, float lambda_init, int causal, void* out,
                  const diffattn_dims* dims, void* stream) {
