@@ -28,7 +28,8 @@ launch stream and reported with its own roofline block:
                       plus the merge kernel;
   backward            diffattn_bwd after the training forward on
                       causal_prefill_bf16 (12 d + 4 dv flops per pair);
-  fp8                 the prefill with Q and K as E4M3 on causal_prefill_bf16;
+  fp8                 the prefill with Q and K as E4M3 on causal_prefill_bf16
+                      and on large_head_bf16;
   proj                the fused Q/K/V projection for causal_prefill_bf16;
   diag                the map diagnostics on the 32K needle workload;
   cpu                 the fp64 CPU oracle on a bounded sample of the headline
@@ -426,6 +427,36 @@ def bench_fp8(w, steps: int, warmup: int):
     return min(t8), min(t16)
 
 
+def fp8_record(w, args, mpk: dict) -> dict:
+    """The fp8 leg on workload w: TFLOP/s of diffattn_fwd_fp8 against the
+    peak of its mix of products.  The scores run on the e4m3 MFMA (dense
+    peak 2x bf16), P.V on the bf16 one, so the mix's peak is the flops over
+    their time at the two peaks.  Per unmasked (query, key) pair the
+    head_dim-128 kernel computes the scores twice (8 d flops: both maps, both
+    sweeps) and one P.V of 2 dv; the head_dim-64 kernel 4 d and 4 dv."""
+    fms, bms16 = bench_fp8(w, max(10, args.steps // 3), max(20, args.warmup // 5))
+    f = w.exec_flops()
+    pairs = f / (4 * (w.d + w.dv))
+    sf, pf = (8 * w.d, 2 * w.dv) if w.d == 128 else (4 * w.d, 4 * w.dv)
+
+    def mix(p):
+        return f / (pairs * (sf / (2 * p) + pf / p))
+
+    kern = "prefill_fp8qk_twopass_kernel" if w.d == 128 else "prefill_fp8qk_kernel"
+    ftf = f / (fms * 1e-3) / 1e12
+    mm = mpk.get("mfma_bf16_tflops")
+    return {
+        "workload": w.name + " (Q, K as e4m3, per-tensor scales)",
+        "value": round(ftf, 2),
+        "unit": "TFLOP/s",
+        "ms_per_call": round(fms, 4),
+        "bf16_ms_per_call_same_run": round(bms16, 4),
+        "speedup_vs_bf16": round(bms16 / fms, 3),
+        "roofline": roofline("mfma", kern, ftf, round(mix(PEAK_BF16_TFLOPS), 1), "TFLOP/s",
+                             mix(mm) if mm else None, _traffic(kern, w.name)),
+    }
+
+
 def bench_proj(w, steps: int, warmup: int):
     """ms per diffattn_qkv_proj launch for workload w's attention shapes
     (d_model = H dv), and ms per library GEMM (torch.matmul) of the same
@@ -613,24 +644,8 @@ def main():
         }
 
     if "fp8" in legs:
-        fms, bms16 = bench_fp8(w2, max(10, args.steps // 3), max(20, args.warmup // 5))
-        # scores on the e4m3 MFMA (peak 2x bf16), P.V on the bf16 one: the
-        # peak of this mix is the flops over their time at the two peaks
-        def mix(p):
-            return f2 / (pairs2 * (4 * w2.d / (2 * p) + 4 * w2.dv / p))
-        ftf = f2 / (fms * 1e-3) / 1e12
-        mm = mpk.get("mfma_bf16_tflops")
-        rec["fp8_qk"] = {
-            "workload": w2.name + " (Q, K as e4m3, per-tensor scales)",
-            "value": round(ftf, 2),
-            "unit": "TFLOP/s",
-            "ms_per_call": round(fms, 4),
-            "bf16_ms_per_call_same_run": round(bms16, 4),
-            "speedup_vs_bf16": round(bms16 / fms, 3),
-            "roofline": roofline("mfma", "prefill_fp8qk_kernel", ftf, round(mix(PEAK_BF16_TFLOPS), 1),
-                                 "TFLOP/s", mix(mm) if mm else None,
-                                 _traffic("prefill_fp8qk_kernel", w2.name)),
-        }
+        for key, wf in (("fp8_qk", w2), ("fp8_qk_large_head", workloads.get("large_head_bf16"))):
+            rec[key] = fp8_record(wf, args, mpk)
 
     if "proj" in legs:
         pms, lms, pflops = bench_proj(w2, max(10, args.steps // 3), max(20, args.warmup // 3))

@@ -112,8 +112,8 @@ int diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
  * Each score is the exact sum of products of the codes (fp32 accumulation)
  * times qk_scales[q] * qk_scales[k] / sqrt(d); the rest of the operator runs
  * as in the bf16 prefill.  Supported: dims->dtype == DIFFATTN_BF16 (the type
- * of v and out) with (head_dim, v_dim) = (64, 128); anything else returns
- * DIFFATTN_ERR_UNSUPPORTED.  Quantising Q and K (choosing the scales,
+ * of v and out) with (head_dim, v_dim) = (64, 128) or (128, 256); anything
+ * else returns DIFFATTN_ERR_UNSUPPORTED.  Quantising Q and K (choosing the scales,
  * rounding to E4M3) is the caller's.
  * Allocates nothing.  Returns a DIFFATTN_* status.
  */

@@ -80,6 +80,8 @@ def entries():
          ("prefill_legs", "large_head_bf16", "ms_per_launch")),
         ("decode_partial_kernel", "decode_bf16", "decode.hip", "a", ("decode", "ms_per_call")),
         ("prefill_fp8qk_kernel", "causal_prefill_bf16", _PREFILL, "b", ("fp8_qk", "ms_per_call")),
+        ("prefill_fp8qk_twopass_kernel", "large_head_bf16", "prefill_twopass.hip", "b",
+         ("fp8_qk_large_head", "ms_per_call")),
         ("qkv_proj_kernel", "causal_prefill_bf16", "proj.hip", "b", ("qkv_proj", "ms_per_call")),
         ("bwd_dq_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
         ("bwd_dkdv_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),

@@ -206,9 +206,9 @@ def fwd_fp8(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tens
             causal: bool = True, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
             pre_norm: bool = False) -> torch.Tensor:
     """Prefill with e4m3 queries and keys: q1, q2, k1, k2 are
-    torch.float8_e4m3fn (or uint8 codes) [B,H,N,64], v bf16 [B,H,Nk,128];
-    qk_scales the four per-tensor dequantisation scales (q1, q2, k1, k2).
-    Returns out [B,H,Nq,128] bf16."""
+    torch.float8_e4m3fn (or uint8 codes) [B,H,N,d], v bf16 [B,H,Nk,dv] with
+    (d, dv) = (64, 128) or (128, 256); qk_scales the four per-tensor
+    dequantisation scales (q1, q2, k1, k2).  Returns out [B,H,Nq,dv] bf16."""
     qs = (q1, q2, k1, k2)
     _require(all(t.dtype in (torch.float8_e4m3fn, torch.uint8) for t in qs),
              "q1, q2, k1, k2 must be float8_e4m3fn (or uint8 codes)")

@@ -228,7 +228,8 @@ int diffattn_fwd_fp8(const void* q1, const void* q2, const void* k1, const void*
         if (!(qk_scales[i] > 0.f) || !isfinite(qk_scales[i])) return DIFFATTN_ERR_INVALID;
     const float s1 = qk_scales[0] * qk_scales[2], s2 = qk_scales[1] * qk_scales[3];
     if (!(s1 > 0.f) || !isfinite(s1) || !(s2 > 0.f) || !isfinite(s2)) return DIFFATTN_ERR_INVALID;
-    if (dims->dtype != DIFFATTN_BF16 || dims->head_dim != 64 || dims->v_dim != 128)
+    if (dims->dtype != DIFFATTN_BF16 || !((dims->head_dim == 64 && dims->v_dim == 128) ||
+                                          (dims->head_dim == 128 && dims->v_dim == 256)))
         return DIFFATTN_ERR_UNSUPPORTED;
     if (causal && dims->seq_q != dims->seq_k) return DIFFATTN_ERR_UNSUPPORTED;
 

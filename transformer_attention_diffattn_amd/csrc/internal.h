@@ -111,13 +111,15 @@ struct DecodeArgs {
 // the supported pairs; the callers have checked that.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
                                hipStream_t stream);
-// Q1, Q2, K1, K2 as OCP e4m3 bytes, V and the output bf16 (d = 64, dv = 128)
+// Q1, Q2, K1, K2 as OCP e4m3 bytes, V and the output bf16 (d, dv = 64, 128 or
+// 128, 256)
 hipError_t launch_prefill_fp8qk(const PrefillArgs& a, int d, int dv, bool causal,
                                 hipStream_t stream);
 hipError_t launch_qkv_proj_bf16(const ProjArgs& a, hipStream_t stream);
-// head_dim 128, v_dim 256: the two-sweep kernel (also the training forward)
-hipError_t launch_prefill_bf16_twopass(const PrefillArgs& a, int d, int dv, bool causal,
-                                       hipStream_t stream);
+// head_dim 128, v_dim 256: the two-sweep kernel (also the training forward);
+// fp8qk: scores from e4m3 queries and keys
+hipError_t launch_prefill_twopass(const PrefillArgs& a, int d, int dv, bool causal, bool fp8qk,
+                                  hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);

@@ -1,6 +1,7 @@
 // Fused Differential Attention prefill for bf16 inputs on gfx950 (CDNA4):
 // the kernels for head_dim 32 and 64, the training forward, and the variant
-// with e4m3 queries and keys (head_dim 128 is in prefill_twopass.hip).  The kernel body is prefill_items in
+// with e4m3 queries and keys (head_dim 128, in both forms, is in
+// prefill_twopass.hip).  The kernel body is prefill_items in
 // prefill_core.h; this file is compiled with the MFMA accumulators in
 // ordinary VGPRs, where the softmax reads the scores without a copy.
 
@@ -63,13 +64,14 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, int dv, bool causal,
                                hipStream_t stream) {
     if (d == 32 && dv == 64) return launch_dims<32, 64, false>(a, causal, stream);
     if (d == 64 && dv == 128) return launch_dims<64, 128, false>(a, causal, stream);
-    if (d == 128 && dv == 256) return launch_prefill_bf16_twopass(a, d, dv, causal, stream);
+    if (d == 128 && dv == 256) return launch_prefill_twopass(a, d, dv, causal, false, stream);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_fp8qk(const PrefillArgs& a, int d, int dv, bool causal,
                                 hipStream_t stream) {
     if (d == 64 && dv == 128) return launch_dims<64, 128, true>(a, causal, stream);
+    if (d == 128 && dv == 256) return launch_prefill_twopass(a, d, dv, causal, true, stream);
     return hipErrorInvalidValue;
 }
 

@@ -52,6 +52,12 @@
 // key 16 (r/8) + 8 (l/32) + r%8 of query l%32 and registers 8c .. 8c+7 are
 // the B operand P^T of keys 16c ..; V^T comes from ds_read_b64_tr_b16.
 //
+// With e4m3 queries and keys (prefill_fp8qk_twopass_kernel, the low-bit
+// variant of "Throughput and Hardware Realities"), the scores of a tile are
+// two v_mfma_scale_f32_32x32x64_f8f6f4 products (unit block scales; the
+// per-tensor scales multiply the exponent's scale), a K row is 128 bytes and
+// a K stage 8 KB; the weights, P and the P.V product are as above.
+//
 // Tiles stream through two 4-stage LDS rings (K1 and K2 of a tile in one
 // 16 KB stage, V in another), filled by buffer loads with the LDS
 // destination (no registers, no LDS store instructions), three tiles ahead
@@ -84,6 +90,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 512;
@@ -95,23 +102,35 @@ constexpr int kBr = 32 * kBlocks;
 constexpr int kNKB = kD / 16;            // score products per tile (k = 16 each)
 constexpr int kNDB = kDV / 2 / 32;       // channel blocks of a wave's half of dv
 constexpr int kStages = 4;               // K ring and V ring
-constexpr int kKRow = 2 * kD;            // bytes per K row
 constexpr int kVRow = 2 * kDV;           // bytes per V row
-constexpr int kKTile = kBc * kKRow;      // 8 KB, one map
-constexpr int kKStage = 2 * kKTile;      // K1 then K2
 constexpr int kVStage = kBc * kVRow;     // 16 KB
-constexpr int kVRing = kStages * kKStage;             // 64 KB
-constexpr int kXchg = kVRing + kStages * kVStage;     // 128 KB
 constexpr int kXchgWave = 64 * 32;                    // 16 fp16 per lane
 constexpr int kXchgSlot = (kThreads / 64) * kXchgWave;
-constexpr int kSmem = kXchg + 2 * kXchgSlot;          // 160 KB
-constexpr int kLoads = 2;                // load instructions per wave: K tile, V tile
+constexpr int kVLoads = kVStage / (16 * kThreads);    // V load instructions per wave and tile
 constexpr float kSumLimit = 4096.0f;     // lazy-maximum bound on a lane's partial tile sum
 constexpr int kXScale = 15;              // exchanged weights are a * 2^15
 constexpr int kBufferDword3 = 0x00020000;
 
-static_assert(kKStage == 1024 * 16 && kVStage == 1024 * 16,
-              "a stage is 1024 16-byte chunks: two load instructions per wave");
+// The K side, by operand format: bf16 (F8 = false) or e4m3 queries and keys
+// (one byte per element, per-tensor scales; the scores then run on
+// v_mfma_scale_f32_32x32x64_f8f6f4, two products per tile instead of eight).
+template <bool F8>
+struct KSide {
+    static constexpr int kRow = F8 ? kD : 2 * kD;        // bytes per Q or K row
+    static constexpr int kCpr = kRow / 16;               // 16-byte chunks per row
+    static constexpr int kTile = kBc * kRow;             // one map's K tile
+    static constexpr int kStage = 2 * kTile;             // K1 then K2
+    static constexpr int kLoads = kStage / (16 * kThreads);
+    static constexpr int kVRing = kStages * kStage;      // V ring start
+    static constexpr int kXchg = kVRing + kStages * kVStage;
+    static constexpr int kSmem = kXchg + 2 * kXchgSlot;  // 160 KB (bf16), 128 KB (e4m3)
+    static constexpr int kNKS = F8 ? kD / 64 : kD / 16;  // score products per tile
+    static constexpr int kOps = F8 ? 2 * kNKS : kNKS;    // 16-byte K operand reads per tile
+    static_assert(kStage % (16 * kThreads) == 0, "a K stage splits into whole loads per wave");
+    // chunk swizzle of a K row: 16 chunks (one pass over the 64 banks) or 8
+    static __device__ __forceinline__ int swz(int r) { return F8 ? (r >> 1) & 7 : r & 15; }
+};
+static_assert(kVStage == kVLoads * 16 * kThreads, "a V stage splits into whole loads per wave");
 
 __device__ __forceinline__ int swap23(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -166,9 +185,7 @@ __device__ __forceinline__ void combine(const u32x4 (&own)[2], const u32x4 (&oth
     }
 }
 
-// chunk swizzles: a K row is 16 chunks of 16 bytes (one full pass over the 64
-// banks), a V row 32
-__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+// chunk swizzle of a V row (32 chunks); K rows: KSide::swz
 __device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
 
 template <bool B>
@@ -176,9 +193,12 @@ using bool_c = std::integral_constant<bool, B>;
 
 // FLAT: each (batch, head) slice of K and V spans < 2 GiB (one descriptor per
 // tensor); SAVE: training forward, also writes D and the log-sum-exp rows.
-template <bool CAUSAL, bool FLAT, bool SAVE>
+template <bool CAUSAL, bool FLAT, bool SAVE, bool F8>
 __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+    using KS = KSide<F8>;
+    constexpr int kKRow = KS::kRow, kKTile = KS::kTile, kKStage = KS::kStage;
+    constexpr int kVRing = KS::kVRing, kXchg = KS::kXchg;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[KS::kSmem];
 
     const int BH = a.B * a.H;
     const int nqt = (a.Nq + kBr - 1) / kBr;
@@ -209,26 +229,43 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
 
     // Q fragments of the wave's map as B operands: column = query, k-slots =
     // channels 16 kb + 8 lh ..
-    bf16x8 qf[kNKB];
+    // (e4m3: k-step s of 64 bytes, this lane's bytes 64 s + 32 lh .. + 31)
+    bf16x8 qf[F8 ? 1 : kNKB];
+    i32x8 qf8[F8 ? kD / 64 : 1];
+    if constexpr (F8) {
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb)
-        qf[kb] = qrow < a.Nq ? *(const bf16x8*)(gq + (size_t)qrow * kKRow + 2 * (16 * kb + 8 * lh))
-                             : bf16x8{};
+        for (int ks = 0; ks < kD / 64; ++ks)
+            qf8[ks] = qrow < a.Nq ? *(const i32x8*)(gq + (size_t)qrow * kKRow + 64 * ks + 32 * lh)
+                                  : i32x8{};
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < kNKB; ++kb)
+            qf[kb] = qrow < a.Nq ? *(const bf16x8*)(gq + (size_t)qrow * kKRow + 2 * (16 * kb + 8 * lh))
+                                 : bf16x8{};
+    }
 
     const int nkt_all = (a.Nk + kBc - 1) / kBc;
     const int nkt = CAUSAL ? min(nkt_all, (qt * kBr + kBr + kBc - 1) / kBc) : nkt_all;
     const int nfull = __builtin_amdgcn_readfirstlane(CAUSAL ? min(a.Nk / kBc, (wq0 + 1) / kBc) : a.Nk / kBc);
 
     // ---- tile loads: global -> LDS ring, buffer_load_dwordx4 ... lds ----
-    // A stage is 1024 chunks; load instruction i of wave w covers chunk
-    // positions 64 (w + 8 i) .. + 63.  K stage: instruction i reads K_{i+1}
-    // (rows 4w .. 4w+3 of that map's tile); V stage: rows 2 (w + 8 i), + 1.
+    // Load instruction i of wave w covers the stage's chunk positions
+    // 64 (w + 8 i) .. + 63.  K stage (K1's tile, then K2's): which map that
+    // is follows from the position (bf16: instruction i reads K_{i+1};
+    // e4m3: waves 0-3 K1, 4-7 K2); V stage: rows 2 (w + 8 i), + 1.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int kpos = 64 * wave_u + lane;
-    const int k_ld_off = (kpos >> 4) * kKRow + 16 * ((kpos & 15) ^ k_swz(kpos >> 4));
-    int v_ld_off[kLoads];
+    int k_ld_off[KS::kLoads], k_src[KS::kLoads];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < KS::kLoads; ++i) {
+        const int pos = 64 * (wave_u + 8 * i) + lane;  // chunk position in the stage
+        const int q = pos % (kKTile / 16);
+        const int row = q / KS::kCpr;
+        k_src[i] = __builtin_amdgcn_readfirstlane(pos / (kKTile / 16));  // 0: K1, 1: K2
+        k_ld_off[i] = row * kKRow + 16 * ((q % KS::kCpr) ^ KS::swz(row));
+    }
+    int v_ld_off[kVLoads];
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
         const int vpos = 64 * (wave_u + 8 * i) + lane;
         v_ld_off[i] = (vpos >> 5) * kVRow + 16 * ((vpos & 31) ^ v_swz(vpos >> 5));
     }
@@ -251,16 +288,17 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
         const bool real = s < 2 * nkt;
         const uint32_t st_off = (uint32_t)(s & (kStages - 1)) * kKStage;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
+        for (int i = 0; i < KS::kLoads; ++i) {
             const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-                smem_base + st_off + (uint32_t)(i * kKTile + 16 * 64 * wave_u));
+                smem_base + st_off + (uint32_t)(16 * 64 * (wave_u + 8 * i)));
             if constexpr (FLAT) {
-                const int voff = k_ld_off + (real ? kt * kKTile : (int)kbytes);
-                load_lds(m0, voff, i == 0 ? rs_k1 : rs_k2);
+                const int voff = k_ld_off[i] + (real ? kt * kKTile : (int)kbytes);
+                load_lds(m0, voff, k_src[i] == 0 ? rs_k1 : rs_k2);
             } else {
                 const int64_t key0 = (int64_t)kt * kBc;
                 const int64_t left = real ? (int64_t)a.Nk - key0 : 0;
-                load_lds(m0, k_ld_off, sgpr_rsrc((i == 0 ? gk1 : gk2) + key0 * kKRow, left * kKRow));
+                load_lds(m0, k_ld_off[i],
+                         sgpr_rsrc((k_src[i] == 0 ? gk1 : gk2) + key0 * kKRow, left * kKRow));
             }
         }
     };
@@ -270,7 +308,7 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
         const bool real = j < nkt;
         const uint32_t st_off = kVRing + (uint32_t)((nkt + j) & (kStages - 1)) * kVStage;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
+        for (int i = 0; i < kVLoads; ++i) {
             const uint32_t m0 = __builtin_amdgcn_readfirstlane(
                 smem_base + st_off + (uint32_t)(16 * 64 * (wave_u + 8 * i)));
             if constexpr (FLAT) {
@@ -291,10 +329,15 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
 
     // ---- operands ----
     const int krow = swap23(l32);
-    int k_off[kNKB];
+    // this lane's 16-byte pieces of its map's K tile (A operand, row krow):
+    // bf16, piece kb = channels 16 kb + 8 lh ..; e4m3, pieces 2 s, 2 s + 1 =
+    // bytes 64 s + 32 lh .. + 31 of k-step s
+    int k_off[KS::kOps];
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb)
-        k_off[kb] = map * kKTile + krow * kKRow + 16 * ((2 * kb + lh) ^ k_swz(krow));
+    for (int kb = 0; kb < KS::kOps; ++kb) {
+        const int ch = F8 ? 4 * (kb >> 1) + 2 * lh + (kb & 1) : 2 * kb + lh;
+        k_off[kb] = map * kKTile + krow * kKRow + 16 * (ch ^ KS::swz(krow));
+    }
     auto k_operand = [&](int st, int kb) {
         return *(const bf16x8*)(smem + st * kKStage + k_off[kb]);
     };
@@ -328,7 +371,8 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
     // key tile of sequence entry s
     auto tile_of = [&](int s) { return s < nkt ? s : s - nkt; };
 
-    const float sl2 = a.scale_log2;
+    // e4m3: the product of the map's two dequantisation scales folds into exp2's
+    const float sl2 = F8 ? a.scale_log2 * a.qk_scale[map] : a.scale_log2;
     float m, l = 0.f;
     f32x16 o[kNDB];
 #pragma unroll
@@ -341,20 +385,39 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
     issue_k(1);
     // the compiler waits for the Q loads by counting its own loads only, which
     // also drains the tile loads issued so far (they are needed first anyway)
+    if constexpr (F8) {
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb) asm volatile("" ::"v"(qf[kb]));
+        for (int ks = 0; ks < kD / 64; ++ks) asm volatile("" ::"v"(qf8[ks]));
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < kNKB; ++kb) asm volatile("" ::"v"(qf[kb]));
+    }
     issue_k(2);
     issue_k(3);
     __syncthreads();
 
     f32x16 sa, sb;  // score tiles: sequence entry s lives in sa for even s, sb for odd
     auto scores = [&](int st, f32x16& s) {
-        bf16x8 ka[kNKB];
+        bf16x8 ka[KS::kOps];
 #pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb) ka[kb] = k_operand(st, kb);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+        for (int kb = 0; kb < KS::kOps; ++kb) ka[kb] = k_operand(st, kb);
+        if constexpr (F8) {
 #pragma unroll
-        for (int kb = 1; kb < kNKB; ++kb) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb], qf[kb], s, 0, 0, 0);
+            for (int ks = 0; ks < kD / 64; ++ks) {
+                const i32x8 ka8 = __builtin_bit_cast(
+                    i32x8, __builtin_shufflevector(__builtin_bit_cast(i32x4, ka[2 * ks]),
+                                                   __builtin_bit_cast(i32x4, ka[2 * ks + 1]), 0, 1,
+                                                   2, 3, 4, 5, 6, 7));
+                // e4m3 A and B (format 0), unit block scales (127 = 2^0)
+                s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka8, qf8[ks], ks == 0 ? f32x16{} : s,
+                                                                    0, 0, 0, 127, 0, 127);
+            }
+        } else {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+            for (int kb = 1; kb < kNKB; ++kb)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb], qf[kb], s, 0, 0, 0);
+        }
     };
     scores(0, sa);
     if (nfull < 1) mask(0, sa);
@@ -395,7 +458,7 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
         l += tsum;
         issue_k(g + 4);
         if (tile_of(g + 1) >= nfull) mask(tile_of(g + 1), nxt);
-        wait_loads(std::integral_constant<int, 2 * kLoads>{});
+        wait_loads(std::integral_constant<int, 2 * KS::kLoads>{});
         __syncthreads();
     };
     int g = 0;
@@ -476,7 +539,7 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
         if constexpr (NEXT) {
             if (j + 1 >= nfull) mask(j + 1, nxt);
         }
-        wait_loads(std::integral_constant<int, 3 * kLoads>{});
+        wait_loads(std::integral_constant<int, 2 * KS::kLoads + kVLoads>{});
         __syncthreads();
     };
     const bool_c<true> T;
@@ -617,18 +680,24 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
 
 template <bool CAUSAL, bool FLAT>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_twopass_kernel(PrefillArgs a) {
-    twopass_items<CAUSAL, FLAT, false>(a);
+    twopass_items<CAUSAL, FLAT, false, false>(a);
 }
 
 template <bool CAUSAL, bool FLAT>
 __global__ __launch_bounds__(kThreads) void prefill_train_twopass_kernel(PrefillArgs a) {
-    twopass_items<CAUSAL, FLAT, true>(a);
+    twopass_items<CAUSAL, FLAT, true, false>(a);
+}
+
+// Scores from e4m3 queries and keys (per-tensor scales in a.qk_scale).
+template <bool CAUSAL, bool FLAT>
+__global__ __launch_bounds__(kThreads) void prefill_fp8qk_twopass_kernel(PrefillArgs a) {
+    twopass_items<CAUSAL, FLAT, false, true>(a);
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16_twopass(const PrefillArgs& a, int d, int dv, bool causal,
-                                       hipStream_t stream) {
+hipError_t launch_prefill_twopass(const PrefillArgs& a, int d, int dv, bool causal, bool fp8qk,
+                                  hipStream_t stream) {
     if (d != kD || dv != kDV) return hipErrorInvalidValue;
     const int nqt = (a.Nq + kBr - 1) / kBr;
     const int64_t items = (int64_t)nqt * a.B * a.H;
@@ -640,7 +709,13 @@ hipError_t launch_prefill_bf16_twopass(const PrefillArgs& a, int d, int dv, bool
     // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
     const bool flat = (int64_t)a.Nk * kVRow + 64 * 1024 < (int64_t)0x7fffffff;
     const void* fn;
-    if (a.lse)
+    if (fp8qk) {
+        if (a.lse) return hipErrorInvalidValue;  // no training forward from e4m3 scores
+        fn = causal ? (flat ? (const void*)prefill_fp8qk_twopass_kernel<true, true>
+                            : (const void*)prefill_fp8qk_twopass_kernel<true, false>)
+                    : (flat ? (const void*)prefill_fp8qk_twopass_kernel<false, true>
+                            : (const void*)prefill_fp8qk_twopass_kernel<false, false>);
+    } else if (a.lse)
         fn = causal ? (flat ? (const void*)prefill_train_twopass_kernel<true, true>
                             : (const void*)prefill_train_twopass_kernel<true, false>)
                     : (flat ? (const void*)prefill_train_twopass_kernel<false, true>
