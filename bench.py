@@ -27,7 +27,8 @@ launch stream and reported with its own roofline block:
   decode_split        the same with 4 splits per (batch, head): partials
                       plus the merge kernel;
   backward            diffattn_bwd after the training forward on
-                      causal_prefill_bf16 (12 d + 4 dv flops per pair);
+                      causal_prefill_bf16 and on large_head_bf16 (12 d + 4 dv
+                      flops per pair);
   fp8                 the prefill with Q and K as E4M3 on causal_prefill_bf16
                       and on large_head_bf16;
   proj                the fused Q/K/V projection for causal_prefill_bf16;
@@ -427,6 +428,28 @@ def bench_fp8(w, steps: int, warmup: int):
     return min(t8), min(t16)
 
 
+def backward_record(w, args, mpk: dict) -> dict:
+    """The backward leg on workload w: diffattn_bwd after the training
+    forward, TFLOP/s at 12 d + 4 dv flops per unmasked (query, key) pair (the
+    two score products again, dP, dV, dK_k and dQ_k)."""
+    bms, tfms = bench_backward(w, max(5, args.steps // 5), max(3, args.warmup // 20))
+    pairs = w.exec_flops() / (4 * (w.d + w.dv))
+    bflops = pairs * (12 * w.d + 4 * w.dv)
+    btf = bflops / (bms * 1e-3) / 1e12
+    kern = ("bwd_prep + bwd_dq_ring + bwd_dkdv_ring + bwd_dlam" if w.d == 128
+            else "bwd_prep + bwd_dq + bwd_dkdv + bwd_dlam")
+    return {
+        "workload": w.name,
+        "value": round(btf, 2),
+        "unit": "TFLOP/s",
+        "ms_per_call": round(bms, 4),
+        "flops_per_call": int(bflops),
+        "fwd_train_ms": round(tfms, 4),
+        "roofline": roofline("mfma", kern, btf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                             mpk.get("mfma_bf16_tflops")),
+    }
+
+
 def fp8_record(w, args, mpk: dict) -> dict:
     """The fp8 leg on workload w: TFLOP/s of diffattn_fwd_fp8 against the
     peak of its mix of products.  The scores run on the e4m3 MFMA (dense
@@ -629,19 +652,8 @@ def main():
     f2 = w2.exec_flops()
     pairs2 = f2 / (4 * (w2.d + w2.dv))
     if "backward" in legs:
-        bms, tfms = bench_backward(w2, max(5, args.steps // 5), max(3, args.warmup // 20))
-        bflops = pairs2 * (12 * w2.d + 4 * w2.dv)
-        btf = bflops / (bms * 1e-3) / 1e12
-        rec["backward"] = {
-            "workload": w2.name,
-            "value": round(btf, 2),
-            "unit": "TFLOP/s",
-            "ms_per_call": round(bms, 4),
-            "flops_per_call": int(bflops),
-            "fwd_train_ms": round(tfms, 4),
-            "roofline": roofline("mfma", "bwd_prep + bwd_dq + bwd_dkdv + bwd_dlam", btf,
-                                 PEAK_BF16_TFLOPS, "TFLOP/s", mpk.get("mfma_bf16_tflops")),
-        }
+        for key, wb in (("backward", w2), ("backward_large_head", workloads.get("large_head_bf16"))):
+            rec[key] = backward_record(wb, args, mpk)
 
     if "fp8" in legs:
         for key, wf in (("fp8_qk", w2), ("fp8_qk_large_head", workloads.get("large_head_bf16"))):

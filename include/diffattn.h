@@ -146,14 +146,15 @@ int diffattn_qkv_proj(const void* x, const void* w, int32_t batch, int32_t seq, 
 
 /*
  * Training forward: diffattn_fwd plus what diffattn_bwd needs, for bf16 with
- * (head_dim, v_dim) = (32, 64) or (64, 128) (else DIFFATTN_ERR_UNSUPPORTED).
+ * (head_dim, v_dim) = (32, 64), (64, 128) or (128, 256) (else
+ * DIFFATTN_ERR_UNSUPPORTED).
  * The backward differentiates the same operator: lambda is a learnable scalar
  * (iloveeagents.com, "Mathematical Formula") and the GroupNorm of step 4 on
  * llmbytes.dev ("How Differential Attention Cancels Common-Mode Noise") is
  * there for stable gradients.
  *   out as diffattn_fwd (same flags);
  *   d_save [B][H][seq_q][dv] fp32: D = O1/l1 - lambda O2/l2 before the
- *     GroupNorm;
+ *     GroupNorm (head_dim 128: D = (A1 - lambda A2) V, the same value);
  *   lse [2][B][H][seq_q] fp32: natural-log log-sum-exp of each row of the
  *     scaled scores, map 1 then map 2.
  * All pointers device memory, 16-byte aligned, owned by the caller.
@@ -165,7 +166,7 @@ int diffattn_fwd_train(const void* q1, const void* q2, const void* k1, const voi
                        void* stream);
 
 /*
- * Workspace bytes diffattn_bwd needs (dD in bf16 and two fp32 row terms per
+ * Workspace bytes diffattn_bwd needs (dD in bf16 and six fp32 row terms per
  * query row); 0 when the sizes are invalid or unsupported.
  */
 size_t diffattn_bwd_workspace_size(const diffattn_dims* dims);

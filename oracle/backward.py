@@ -105,6 +105,37 @@ def head_backward(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
     return dq1, dq2, dk1, dk2, dv, dlam
 
 
+def head_magnitudes(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
+                    lambda_init: float = 0.8, eps: float = 1e-5, pre_norm: bool = False):
+    """Per gradient element of one head, the sum of the absolute values of
+    the terms that make it up, one level down the chain rule: with
+    |dA|_ij = sum_c |dD_ic| |V_jc| and delta_k = rowsum(A_k * dA_k),
+      dQ_k: tau c_k sum_j A_k,ij (|dA|_ij + |delta_k,i|) |K_k,jc|,
+      dK_k: tau c_k sum_i A_k,ij (|dA|_ij + |delta_k,i|) |Q_k,ic|,
+      dV:   sum_i (A_1,ij + |lambda| A_2,ij) |dD_ic|,
+    with c_1 = 1, c_2 = |lambda|.  Every gradient is bounded by it in
+    absolute value (the triangle inequality on the expressions of
+    head_backward), and a computation that rounds a factor of each term to a
+    format with unit roundoff u is off by at most a small multiple of u times
+    it: the bound a bf16 kernel is held to where heavy-tailed inputs make a
+    few terms far larger than their sum.  Returns (mq1, mq2, mk1, mk2, mv)."""
+    q1, q2, k1, k2, v, dout = (_f64(t) for t in (q1, q2, k1, k2, v, dout))
+    d = q1.shape[1]
+    tau = 1.0 / np.sqrt(d)
+    a1 = _softmax_rows(_scores(q1, k1, causal))
+    a2 = _softmax_rows(_scores(q2, k2, causal))
+    dD = _norm_backward(a1 @ v - lam * (a2 @ v), dout, lambda_init, eps, pre_norm)
+    da = dD @ v.T
+    absda = np.abs(dD) @ np.abs(v).T
+    out = []
+    for a, c, q, k in ((a1, 1.0, q1, k1), (a2, abs(lam), q2, k2)):
+        delta = (a * da).sum(axis=1, keepdims=True)
+        t = a * (absda + np.abs(delta))
+        out.append((tau * c * (t @ np.abs(k)), tau * c * (t.T @ np.abs(q))))
+    mv = (a1 + abs(lam) * a2).T @ np.abs(dD)
+    return out[0][0], out[1][0], out[0][1], out[1][1], mv
+
+
 def head_dlambda_terms(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
                        lambda_init: float = 0.8, eps: float = 1e-5, pre_norm: bool = False):
     """Per query row of one head: the row's share -O_2 . dD of dlambda and the

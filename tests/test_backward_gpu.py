@@ -23,6 +23,15 @@ Tolerances, from the arithmetic (bf16 operands, fp32 accumulation):
   size of that term, tens of percent.  The per-element bound above catches
   large errors in a few elements, this one small systematic ones;
 * dlambda: 3e-2 relative (a sum over all rows of fp32 row terms).
+* Heavy-tailed inputs (Student-t with 3 degrees of freedom, the large-head
+  workload's): a few keys carry entries a hundred times the typical one, and
+  a gradient element can be a sum of large terms that nearly cancel (seen: a
+  dQ element of 0.03 made of terms near 10, one key's entry at -135).  A bf16
+  factor of each term is rounded (dD, the weights, dS), so the error of such
+  an element scales with the sum of its terms' absolute values, M
+  (oracle.backward.head_magnitudes), not with the tensor's rms: those tests
+  add 2^-7 M (four roundings of 2^-9) to the per-element bound.  The observed
+  worst is ~0.3 2^-9 M; the Frobenius bound is unchanged.
 """
 import numpy as np
 import pytest
@@ -64,13 +73,17 @@ def _gpu(x, dout, causal, pre_norm):
     return out, d_save, lse, grads, plain
 
 
-def _check_grad(name, got, ref):
+def _check_grad(name, got, ref, mag=None):
+    """mag (heavy-tailed inputs only): oracle.backward.head_magnitudes of the
+    same elements, adding 2^-7 mag to the bound (see the module docstring)."""
     got = got.detach().double().cpu().numpy()
     ref = np.asarray(ref, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{name}: non-finite"
     rms = float(np.sqrt((ref ** 2).mean()))
     err = np.abs(got - ref)
     bound = 0.12 * rms + 0.03 * np.abs(ref) + 1e-3
+    if mag is not None:
+        bound = bound + 2.0 ** -7 * np.asarray(mag, dtype=np.float64)
     i = np.unravel_index(np.argmax(err / bound), err.shape)
     assert np.all(err <= bound), (f"{name}: element {i} gpu {got[i]:.5f} oracle {ref[i]:.5f} "
                                   f"(rms {rms:.4f}, max err {err.max():.4f})")
@@ -107,7 +120,11 @@ def _check_dlam(got, ref, noise):
     assert np.all(np.abs(got - ref) <= 3e-2 * np.abs(ref) + floor), (got, ref, floor)
 
 
-@pytest.mark.parametrize("d,dv", [(32, 64), (64, 128)], ids=["d32", "d64"])
+DIMS = [(32, 64), (64, 128), (128, 256)]
+DIM_IDS = ["d32", "d64", "d128"]
+
+
+@pytest.mark.parametrize("d,dv", DIMS, ids=DIM_IDS)
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 @pytest.mark.parametrize("n", [1, 7, 64, 129, 300])
 def test_backward_small(d, dv, causal, n):
@@ -127,7 +144,7 @@ def test_backward_small(d, dv, causal, n):
     _check_dlam(grads[5], ref[5], _dlam_noise(x, dout, causal, False, _all_heads(x)))
 
 
-@pytest.mark.parametrize("d,dv,causal", [(64, 128, True), (32, 64, False)])
+@pytest.mark.parametrize("d,dv,causal", [(64, 128, True), (32, 64, False), (128, 256, True)])
 def test_backward_pre_norm_output(d, dv, causal):
     w, x, dout = _inputs(1, 2, 150, d, dv, causal, seed=77)
     out, d_save, lse, grads, plain = _gpu(x, dout, causal, True)
@@ -139,8 +156,10 @@ def test_backward_pre_norm_output(d, dv, causal):
     _check_dlam(grads[5], ref[5], _dlam_noise(x, dout, causal, True, _all_heads(x)))
 
 
-def test_backward_rectangular_noncausal():
-    B, H, nq, nk, d, dv = 1, 2, 70, 200, 64, 128
+@pytest.mark.parametrize("d,dv,nq,nk", [(64, 128, 70, 200), (128, 256, 70, 200),
+                                         (128, 256, 300, 33)])
+def test_backward_rectangular_noncausal(d, dv, nq, nk):
+    B, H = 1, 2
     w = workloads.Workload("bwd", "prefill", B=B, H=H, nq=nq, nk=nk, d=d, dv=dv, dtype="bf16",
                            causal=False, lam=("uniform", 0.2, 0.9), seed=91)
     x = workloads.make_prefill(w)
@@ -153,8 +172,9 @@ def test_backward_rectangular_noncausal():
     _check_dlam(grads[5], ref[5], _dlam_noise(x, dout, False, False, _all_heads(x)))
 
 
-def test_backward_deterministic():
-    w, x, dout = _inputs(1, 4, 300, 64, 128, True, seed=93)
+@pytest.mark.parametrize("d,dv", [(64, 128), (128, 256)], ids=["d64", "d128"])
+def test_backward_deterministic(d, dv):
+    w, x, dout = _inputs(1, 4, 300, d, dv, True, seed=93)
     a = _gpu(x, dout, True, False)[3]
     b = _gpu(x, dout, True, False)[3]
     for ga, gb in zip(a, b):
@@ -162,7 +182,7 @@ def test_backward_deterministic():
 
 
 def test_backward_rejects_unsupported_and_small_workspace():
-    w, x, dout = _inputs(1, 1, 16, 128, 256, True, seed=94)
+    w, x, dout = _inputs(1, 1, 16, 32, 128, True, seed=94)
     g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
     with pytest.raises(ValueError):
         da.fwd_train(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"], causal=True)
@@ -198,3 +218,55 @@ def test_backward_headline_shape_sampled_heads():
                   for b in range(w.B))
         noise = _dlam_noise(x, dout, True, False, [(b, h) for b in range(w.B)])
         _check_dlam(grads[5][h:h + 1], np.array([tot]), noise)
+
+
+def test_backward_large_head_near_cancellation():
+    """The head_dim-128 regime of the large-head workload at a size the
+    oracle checks in full: Student-t Q/K with 3 degrees of freedom, lambda
+    0.95 (the two maps nearly agree), causal, three query tiles with a ragged
+    end."""
+    w = workloads.Workload("bwd", "prefill", B=1, H=3, nq=333, nk=333, d=128, dv=256,
+                           dtype="bf16", causal=True, dist="student_t3", lam=("const", 0.95),
+                           seed=97)
+    x = workloads.make_prefill(w)
+    dout = torch.randn((1, 3, 333, 256), generator=torch.Generator().manual_seed(98),
+                       dtype=torch.float64).to(torch.bfloat16)
+    out, d_save, lse, grads, plain = _gpu(x, dout, True, False)
+    assert torch.equal(out, plain)
+    ref = obw.backward(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], dout, causal=True)
+    mags = [np.stack([obw.head_magnitudes(x["q1"][0, h], x["q2"][0, h], x["k1"][0, h],
+                                          x["k2"][0, h], x["v"][0, h], 0.95, dout[0, h],
+                                          causal=True)[i] for h in range(3)])[None]
+            for i in range(5)]
+    for name, gg, rr, mm in zip(NAMES, grads[:5], ref[:5], mags):
+        _check_grad(name, gg, rr, mm)
+    _check_dlam(grads[5], ref[5], _dlam_noise(x, dout, True, False, _all_heads(x)))
+
+
+def test_backward_large_head_shape_sampled_heads():
+    """The large-head workload (B2 H32 N8192 d128 dv256, causal, Student-t,
+    lambda 0.95): the GPU computes every head; two heads are checked in full
+    and dlambda of one head over the batch."""
+    w = workloads.get("large_head_bf16")
+    x = workloads.make_prefill(w)
+    dout = torch.randn((w.B, w.H, w.nq, w.dv), generator=torch.Generator().manual_seed(99),
+                       dtype=torch.float64).to(torch.bfloat16)
+    out, d_save, lse, grads, plain = _gpu(x, dout, True, False)
+    grads = [g.cpu() for g in grads]
+    del out, d_save, lse, plain
+    torch.cuda.empty_cache()
+    lam = x["lam"].double().numpy()
+    for (b, h) in [(0, 5), (1, 30)]:
+        hx = (x["q1"][b, h], x["q2"][b, h], x["k1"][b, h], x["k2"][b, h], x["v"][b, h],
+              float(lam[h]), dout[b, h])
+        r = obw.head_backward(*hx, causal=True)
+        m = obw.head_magnitudes(*hx, causal=True)
+        for name, gg, rr, mm in zip(NAMES, grads[:5], r[:5], m):
+            _check_grad(f"{name} b{b} h{h}", gg[b, h], rr, mm)
+        del r, m
+    h = 17
+    tot = sum(obw.head_dlambda_terms(x["q1"][b, h], x["q2"][b, h], x["k1"][b, h], x["k2"][b, h],
+                                     x["v"][b, h], float(lam[h]), dout[b, h], causal=True)[0].sum()
+              for b in range(w.B))
+    noise = _dlam_noise(x, dout, True, False, [(b, h) for b in range(w.B)])
+    _check_dlam(grads[5][h:h + 1], np.array([tot]), noise)

@@ -139,6 +139,39 @@ def test_dlambda_terms_sum_to_dlambda():
         assert np.all(a >= np.abs(r))
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_magnitudes_bound_the_gradients(causal):
+    """Every gradient element is at most its magnitude (the triangle
+    inequality on the terms it sums), for normal and heavy-tailed inputs."""
+    for seed, heavy in ((90, False), (91, True)):
+        c = _case(15, 6, 10, seed)
+        if heavy:
+            rng = np.random.default_rng(seed + 50)
+            for k in ("q1", "k1", "k2"):
+                c[k] = rng.standard_t(3, size=c[k].shape)
+        for lam in (0.8, -0.4, 1.5):
+            g = obw.head_backward(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], lam, c["dout"],
+                                  causal=causal)
+            m = obw.head_magnitudes(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], lam, c["dout"],
+                                    causal=causal)
+            for name, gg, mm in zip(("dq1", "dq2", "dk1", "dk2", "dv"), g[:5], m):
+                assert gg.shape == mm.shape
+                assert np.all(np.abs(gg) <= mm * (1 + 1e-12) + 1e-15), name
+
+
+def test_magnitude_of_dv_is_exact_for_same_sign_terms():
+    """With the output taken before the normalisation, dout >= 0 and
+    lambda <= 0, every term of dV = (A_1 - lambda A_2)^T dD is >= 0, so the
+    magnitude equals dV itself."""
+    c = _case(12, 4, 7, 95)
+    c["dout"] = np.abs(c["dout"])
+    g = obw.head_backward(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], -0.6, c["dout"],
+                          causal=True, pre_norm=True)
+    m = obw.head_magnitudes(c["q1"], c["q2"], c["k1"], c["k2"], c["v"], -0.6, c["dout"],
+                            causal=True, pre_norm=True)
+    np.testing.assert_allclose(m[4], g[4], rtol=1e-12)
+
+
 MUTANTS = [
     ("dv = a1.T @ dD - lam * (a2.T @ dD)", "dv = a1.T @ dD + lam * (a2.T @ dD)"),
     ("da2 = -lam * da1", "da2 = lam * da1"),

@@ -285,7 +285,7 @@ def fwd_train(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
               v: torch.Tensor, lam: Union[float, Sequence[float], torch.Tensor],
               lambda_init: float = 0.8, causal: bool = True, eps: float = 1e-5,
               pre_norm: bool = False):
-    """Training forward (bf16, d = 32 or 64): returns (out, d_save, lse) with
+    """Training forward (bf16, d = 32, 64 or 128): returns (out, d_save, lse) with
     d_save = D [B,H,Nq,dv] fp32 and lse [2,B,H,Nq] fp32 (natural-log
     log-sum-exp of each map's score rows), the inputs of ``bwd``."""
     B, H, Nq, Nk, d, dv = _check_inputs(q1, q2, k1, k2, v)

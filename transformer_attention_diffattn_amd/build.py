@@ -33,13 +33,16 @@ SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=und
 # the roofline microbenchmarks: a library of their own, not part of the operator
 PEAKS_SRC = "peaks.hip"
 PEAKS_LIB = os.path.join(LIBDIR, "libdiffattn_peaks.so")
-SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_twopass.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "diag.hip", "proj.hip"]
+SOURCES = ["api.hip", "prefill_bf16.hip", "prefill_twopass.hip", "prefill_f32.hip", "decode.hip", "backward.hip", "backward_ring.hip", "diag.hip", "proj.hip"]
 # Per-source extra flags.  The narrow-head prefill kernel keeps its score
 # accumulators in ordinary VGPRs, where the softmax reads them without a copy
 # out of the accumulation registers; the compiler's default heuristic would
 # put every matrix accumulator in AGPRs.
 EXTRA_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "prefill_twopass.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "prefill_twopass.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               # builtin products in VGPRs; the accumulators are pinned to
+               # AGPRs by the kernels' own asm
+               "backward_ring.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

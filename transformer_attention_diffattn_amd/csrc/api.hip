@@ -296,7 +296,8 @@ static int check_train_dims(const diffattn_dims* dims, int causal) {
     int st = check_dims(dims);
     if (st != DIFFATTN_OK) return st;
     if (dims->dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
-    if (!((dims->head_dim == 32 && dims->v_dim == 64) || (dims->head_dim == 64 && dims->v_dim == 128)))
+    if (!((dims->head_dim == 32 && dims->v_dim == 64) || (dims->head_dim == 64 && dims->v_dim == 128) ||
+          (dims->head_dim == 128 && dims->v_dim == 256)))
         return DIFFATTN_ERR_UNSUPPORTED;
     if (causal && dims->seq_q != dims->seq_k) return DIFFATTN_ERR_UNSUPPORTED;
     return DIFFATTN_OK;
@@ -373,10 +374,10 @@ int diffattn_bwd(const void* q1, const void* q2, const void* k1, const void* k2,
     a.dk2 = dk2;
     a.dv = dv;
     a.dlam = dlambda;
+    const size_t rows = (size_t)dims->batch * dims->heads * dims->seq_q;
     a.dd = workspace;
-    a.delta = (float*)((char*)workspace +
-                       ((size_t)dims->batch * dims->heads * dims->seq_q * dims->v_dim * 2 + 255) /
-                           256 * 256);
+    a.delta = (float*)((char*)workspace + (rows * dims->v_dim * 2 + 255) / 256 * 256);
+    a.rows = (float*)((char*)a.delta + (2 * rows * sizeof(float) + 255) / 256 * 256);
     a.B = dims->batch;
     a.H = dims->heads;
     a.Nq = dims->seq_q;

@@ -1,5 +1,7 @@
 // Backward of the fused Differential Attention operator for bf16 inputs on
-// gfx950, head_dim 32 or 64 (v_dim 64 or 128).
+// gfx950, head_dim 32 or 64 (v_dim 64 or 128); head_dim 128 (v_dim 256) runs
+// the prep and dlambda kernels here and the dQ and dK/dV kernels of
+// backward_ring.hip.
 //
 // The pages treat the operator as trained: lambda is learnable
 // (iloveeagents.com, "Mathematical Formula") and the per-head GroupNorm with
@@ -515,13 +517,27 @@ hipError_t launch_dims(const BackwardArgs& a, bool causal, hipStream_t stream) {
 
 size_t backward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int dv) {
     const size_t dd = ((size_t)(B * H * Nq * dv * 2) + 255) / 256 * 256;
-    return dd + (size_t)(2 * B * H * Nq) * sizeof(float);
+    const size_t delta = ((size_t)(2 * B * H * Nq) * sizeof(float) + 255) / 256 * 256;
+    return dd + delta + (size_t)(B * H * Nq) * 4 * sizeof(float);
 }
 
 hipError_t launch_backward_bf16(const BackwardArgs& a, int d, int dv, bool causal,
                                 hipStream_t stream) {
     if (d == 32 && dv == 64) return launch_dims<32, 64>(a, causal, stream);
     if (d == 64 && dv == 128) return launch_dims<64, 128>(a, causal, stream);
+    if (d == 128 && dv == 256) {
+        BackwardArgs copy = a;
+        void* args[] = {&copy};
+        const int64_t g_prep = ((int64_t)a.B * a.H * a.Nq + 3) / 4;
+        if (g_prep > 0x7fffffff) return hipErrorInvalidValue;
+        hipError_t e = hipLaunchKernel((const void*)bwd_prep_kernel<256>, dim3((unsigned)g_prep),
+                                       dim3(kBwdThreads), args, 0, stream);
+        if (e != hipSuccess) return e;
+        e = launch_backward_ring(a, causal, stream);
+        if (e != hipSuccess) return e;
+        return hipLaunchKernel((const void*)bwd_dlam_kernel, dim3((unsigned)a.H),
+                               dim3(kBwdThreads), args, 0, stream);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,660 @@
+// dQ and dK/dV kernels of the Differential Attention backward for head_dim
+// 128 and v_dim 256 on gfx950 (CDNA4).
+//
+// The chain rule is that of backward.hip (the pages' operator: iloveeagents.com,
+// "Mathematical Formula", lambda learnable; llmbytes.dev, "How Differential
+// Attention Cancels Common-Mode Noise", step 4), with tau = 1/sqrt(d):
+//   dP = dD V^T,  delta_k = rowsum(A_k * dP),
+//   dS_1 = A_1 (dP - delta_1),  dS_2 = -lambda A_2 (dP - delta_2),
+//   dQ_k = tau dS_k K_k,  dK_k = tau dS_k^T Q_k,  dV = (A_1 - lambda A_2)^T dD.
+// A_k = exp(S_k tau - lse_k) from the training forward's log-sum-exp.
+//
+// Why a kernel of its own.  At head_dim 128 a wave that owns 32 rows and both
+// maps holds 128 registers of resident operands (both maps' Q or K columns and
+// dD or V columns) and up to 256 of accumulators (dK/dV: dV over 256
+// channels and both dK_k; dQ: both dQ_k).  That fits one wave per SIMD with
+// its 512 registers (accumulators in the AGPRs), and at this head size a
+// tile carries 48-64 products (1,536-2,048 MFMA cycles) against ~200 vector
+// instructions, so one wave keeps the matrix core fed if its operands arrive
+// in time.  Both maps in one wave also compute dP once for the two.
+//
+//   dq    workgroup = 128 query rows of one (batch, head), wave w rows
+//         32 w .. 32 w + 31 of both maps; sweeps the key tiles twice.  Per
+//         tile, both sweeps: S_k^T = K_k Q_k^T (2 x 8 products) and
+//         dP^T = V dD^T (16); sweep 1 sums delta_k = rowsum(A_k * dP),
+//         sweep 2 forms dS_k = A_k (dP - delta_k) in fp32 and accumulates
+//         dQ_k^T += K_k^T dS_k^T (2 x 8).  Writes dQ_k, delta_k and the row
+//         terms of the dK/dV kernel.  dD of the workgroup's rows sits in LDS
+//         (64 KB) beside a 3-stage ring.
+//   dkdv  workgroup = 128 keys, wave w keys 32 w .. of both maps; sweeps the
+//         query tiles.  Per tile: S_k = Q_k K_k^T (2 x 8), dP = dD V^T (16),
+//         dV^T += dD^T W with W = A_1 - lambda A_2 (16), dK_k^T += Q_k^T dS_k
+//         (2 x 8).
+//
+// Tiles of 32 rows stream through a 4-stage LDS ring, three tiles ahead, by
+// buffer loads with the LDS destination (no registers, no LDS stores).  Each
+// tile is read both as rows (16-byte reads: the A operand of the score and
+// dP products, rows in swap23 order so that score accumulators are the next
+// product's B operands) and as columns (ds_read_b64_tr_b16: the transposed
+// A operand of the X, Y, dV and dK products).  One XOR swizzle of a row's
+// 16-byte chunks serves both: chunk c of row r sits at position
+// c ^ (4 (r mod 4) + (r / 4) mod 4), which puts the 16 rows of a row read
+// and the 4 rows x 4 chunks of a transposing read on 64 distinct banks.
+
+#include "internal.h"
+#include "tile_ops.h"
+
+#include <math.h>
+
+namespace diffattn {
+namespace {
+
+using namespace tile;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128, kDV = 256;
+constexpr int kKRow = 2 * kD;      // bytes per Q or K row
+constexpr int kVRow = 2 * kDV;     // bytes per V or dD row
+constexpr int kNKB = kD / 16;      // k = 16 steps over d
+constexpr int kNVB = kDV / 16;     // k = 16 steps over dv
+constexpr int kNCB = kD / 32;      // 32-row blocks of d
+constexpr int kNDB = kDV / 32;     // 32-row blocks of dv
+constexpr int kKTile = 32 * kKRow;  // 8 KB
+constexpr int kVTile = 32 * kVRow;  // 16 KB
+constexpr int kStages = 4;
+constexpr int kRowsWG = 128;        // rows (dq) or keys (dkdv) of a workgroup
+constexpr int kTileLoads = (2 * kKTile + kVTile) / (16 * kBwdThreads);  // per wave and tile
+constexpr int kStage = 2 * kKTile + kVTile;  // 32 KB: X1 | X2 | Y tiles
+constexpr int kDqBlock = kRowsWG * kVRow;     // 64 KB: dD of the dQ workgroup's rows
+constexpr int kDqBlockLoads = kDqBlock / (16 * kBwdThreads);
+constexpr int kDqStages = 3;                 // dQ ring (the dD block takes the rest)
+constexpr int kRowSlot = 1024;      // a wave's copy of a tile's row terms (dK/dV)
+constexpr int kRowStage = 4 * kRowSlot;
+static_assert(kStage == 32 * 1024, "stage bases must leave the in-tile address bits free");
+constexpr int kBufferDword3 = 0x00020000;
+
+static_assert(kTileLoads * 16 * kBwdThreads == 2 * kKTile + kVTile, "whole loads per wave");
+static_assert(kKTile % (16 * kBwdThreads) == 0, "a load instruction stays in one tile");
+
+__device__ __forceinline__ int rswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// LDS addressing.  Every tile sits at a fixed offset in its ring stage and a
+// stage's base is a multiple of 32 KB, while a read's address within a tile
+// is below 16 KB, so the address of a read is
+//     (lane base | stage base) ^ (bits of the k step or column block)
+// plus an immediate (the tile, the k step of a transposed read): the swizzle
+// is an XOR on the chunk index, and the bits a read's position adds to the
+// lane's own are disjoint from the lane's row bits.  One instruction per read
+// and no register per read; the per-tile base goes through an empty asm so
+// that the compiler forms each address from it rather than keeping one
+// register per (read, lane) across the loop.
+
+// Row reads (A operand rows, 16 bytes at elements k0 + 8 lh of row `row`):
+// lane base for RB-byte rows; the read of k step kb (k0 = 16 kb) is at
+// base ^ (32 kb).
+template <int RB>
+__device__ __forceinline__ int row_base(int row, int lh) {
+    return row * RB + 16 * (lh ^ rswz(row));
+}
+
+// Transposed reads (A operand column cb + l32 over rows k0 + 8 lh .. + 7,
+// two ds_read_b64_tr_b16 of rows +0..3 and +4..7): lane base of the first
+// for RB-byte rows; the read of column block cbk (cb = 32 cbk) and rows
+// k0 = 16 kk is at (base ^ (64 cbk)) + 16 kk RB.  Within a 16-lane group,
+// lane 4e + r addresses row e at column base + 4r and receives column
+// base + (lane % 16) of the 4 rows.
+template <int RB>
+__device__ __forceinline__ int col_base(int lane) {
+    const int g = lane >> 4, e = (lane & 15) >> 2, r = lane & 3;
+    const int w = 2 * (g & 1) + (r >> 1), z = 2 * (g >> 1);
+    return (8 * (g >> 1) + e) * RB + 64 * e + 16 * (w ^ z) + 8 * (r & 1);
+}
+
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+template <int IMM>
+__device__ __forceinline__ bf16x8 lds_row(const uint8_t* smem, int addr) {
+    return *(const bf16x8*)(smem + addr + IMM);
+}
+
+// The half-1 base of a transposed read is the half-0 base four rows on with
+// bit 4 flipped (z and hence w ^ z differ in bit 0): a1 = (a0 ^ 16) + 4 RB.
+template <int RB, int IMM>
+__device__ __forceinline__ bf16x8 lds_col(const uint8_t* smem, int a0) {
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_u8*)(smem + a0 + IMM));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(lds_u8*)(smem + (a0 ^ 16) + 4 * RB + IMM));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Raw buffer descriptor of `bytes` bytes from `base` (wave-uniform): loads
+// past the end return zeros and touch no memory.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, int64_t bytes) {
+    const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffff));
+    r[2] = __builtin_amdgcn_readfirstlane((int)n);
+    r[3] = kBufferDword3;
+    return r;
+}
+
+// 16 bytes per lane from global memory to LDS at m0 + 16 lane
+__device__ __forceinline__ void load_lds(uint32_t m0, int voff, i32x4 rsrc) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// acc += a b with the accumulator held in AGPRs for the whole sweep.  The
+// compiler's builtin may place (and move) an accumulator in either register
+// file; with 256 accumulator registers per wave that costs copies and
+// spills, so these products are written out.  Two hazards are the code's own
+// to cover, since the compiler does not look into the statement: an operand
+// written by a vector instruction needs 2 wait states before the product
+// reads it (the leading s_nop 1), and the accumulators are read back only
+// after settle().  Volatile keeps the products in program order.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// After the last mfma_acc: the products' latency (at most 16 passes) passes
+// before any accumulator is read by another instruction.
+template <int N>
+__device__ __forceinline__ void settle(f32x16 (&acc)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+}
+__device__ __forceinline__ void settle_wait() {
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One 32-row tile of the two 128-wide tensors X1, X2 ([n][128] bf16) and
+// the 256-wide Y ([n][256] bf16) into a ring stage laid out X1 | X2 | Y.
+// Load instruction i of wave w fills chunk positions 256 i + 64 w .. + 63 of
+// the stage (i < 2: X1, i < 4: X2, else Y); each lane fetches the chunk that
+// the swizzle puts at its position.  Worked out, the source offsets of a
+// lane are one X offset (instruction i = 1 and 3 add 16 rows, 4096 bytes)
+// and one Y offset XORed with a wave-uniform 16 ((2 (i - 4) + w / 2) mod 4)
+// (instruction i >= 4 starts 8 (i - 4) rows, 4096 (i - 4) bytes, further):
+// two registers per lane.
+struct TileFeed {
+    int offx, offy;
+    __device__ __forceinline__ void init(int wave, int lane) {
+        const int lh = lane >> 5;
+        const int xr = 4 * wave + (lane >> 4);  // row of instruction 0
+        offx = xr * kKRow + 16 * ((lane & 15) ^ rswz(xr));
+        const int yr = 2 * wave + lh;  // row of instruction 4
+        offy = yr * kVRow + 16 * ((lane & 31) ^ (4 * (yr & 3)));
+    }
+    // rows row0 .. row0 + 31 of tensors with n rows
+    __device__ __forceinline__ void issue(uint32_t stage, int wave, const uint8_t* x1,
+                                          const uint8_t* x2, const uint8_t* y, int64_t row0,
+                                          int64_t n) const {
+        const int64_t left = n - row0;
+        const i32x4 r1 = sgpr_rsrc(x1 + row0 * kKRow, left * kKRow);
+        const i32x4 r2 = sgpr_rsrc(x2 + row0 * kKRow, left * kKRow);
+        const i32x4 ry = sgpr_rsrc(y + row0 * kVRow, left * kVRow);
+#pragma unroll
+        for (int i = 0; i < kTileLoads; ++i) {
+            const uint32_t m0 =
+                __builtin_amdgcn_readfirstlane(stage + (uint32_t)(16 * (256 * i + 64 * wave)));
+            // (the row steps go into the per-lane offset, which the
+            // descriptor's range check covers)
+            if (i < 4) {
+                load_lds(m0, offx + (i & 1) * 16 * kKRow, i < 2 ? r1 : r2);
+            } else {
+                const int b = 16 * ((2 * (i - 4) + (wave >> 1)) & 3);
+                load_lds(m0, (offy ^ b) + (i - 4) * 8 * kVRow, ry);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// dQ_1, dQ_2, delta_1, delta_2 and the row terms
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_ring_kernel(BackwardArgs a) {
+    // dD of the workgroup's 128 rows (64 KB), then a 3-stage ring of K1 | K2 | V
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kDqBlock + kDqStages * kStage];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int BH = a.B * a.H;
+    const int nqt = (a.Nq + kRowsWG - 1) / kRowsWG;
+    const int t = blockIdx.x / BH;  // longest causal tiles first
+    const int bh = blockIdx.x - t * BH;
+    const int qt = CAUSAL ? nqt - 1 - t : t;
+    const int h = bh % a.H;
+    const int qw0 = __builtin_amdgcn_readfirstlane(qt * kRowsWG + 32 * wave_u);
+    const int qrow = qw0 + l32;
+    const bool qok = qrow < a.Nq;
+
+    const uint8_t* gq1 = (const uint8_t*)a.q1 + (size_t)bh * a.Nq * kKRow;
+    const uint8_t* gq2 = (const uint8_t*)a.q2 + (size_t)bh * a.Nq * kKRow;
+    const uint8_t* gk1 = (const uint8_t*)a.k1 + (size_t)bh * a.Nk * kKRow;
+    const uint8_t* gk2 = (const uint8_t*)a.k2 + (size_t)bh * a.Nk * kKRow;
+    const uint8_t* gv = (const uint8_t*)a.v + (size_t)bh * a.Nk * kVRow;
+    const uint8_t* gdd = (const uint8_t*)a.dd + (size_t)bh * a.Nq * kVRow;
+
+    // B operands of this lane's query (column l32): Q_k^T over d (dD^T over
+    // dv is read from the LDS block each tile)
+    bf16x8 q1f[kNKB], q2f[kNKB];
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb) {
+        const size_t o = (size_t)qrow * kKRow + 2 * (16 * kb + 8 * lh);
+        q1f[kb] = qok ? *(const bf16x8*)(gq1 + o) : bf16x8{};
+        q2f[kb] = qok ? *(const bf16x8*)(gq2 + o) : bf16x8{};
+    }
+    // keys visible to this lane's query: 0 .. key_end - 1
+    const int key_end = qok ? (CAUSAL ? min(a.Nk, qrow + 1) : a.Nk) : 0;
+    const float lse1 = qok ? a.lse[(size_t)bh * a.Nq + qrow] * kLog2e : 0.f;
+    const float lse2 = qok ? a.lse[((size_t)BH + bh) * a.Nq + qrow] * kLog2e : 0.f;
+    const float sl2 = a.scale_log2;
+    // The compiler counts only its own loads when it waits for these, so a
+    // first use inside the loop would wait for the ring's loads as well (on
+    // every tile).  Used here, before the ring starts, they are complete.
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb) asm volatile("" ::"v"(q1f[kb]), "v"(q2f[kb]));
+    asm volatile("" ::"v"(lse1), "v"(lse2));
+
+    f32x16 dq1[kNCB], dq2[kNCB];
+#pragma unroll
+    for (int cb = 0; cb < kNCB; ++cb) dq1[cb] = dq2[cb] = f32x16{};
+    float dsum1 = 0.f, dsum2 = 0.f;
+
+    const int nkt_all = (a.Nk + 31) / 32;
+    const int nkt = CAUSAL ? min(nkt_all, (qt * kRowsWG + kRowsWG + 31) / 32) : nkt_all;
+    // key tiles in which some key is visible to some row of this wave
+    const int nkt_w = CAUSAL ? min(nkt, (qw0 + 31) / 32 + 1) : nkt;
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+    TileFeed feed;
+    feed.init(wave_u, lane);
+    {
+        // the dD block: 16 loads per wave, row 8 i + 2 w + lane / 32 in
+        // instruction i (the Y part of the tile feed, continued)
+        const int64_t row0 = (int64_t)qt * kRowsWG;
+        const i32x4 rd = sgpr_rsrc(gdd + row0 * kVRow, ((int64_t)a.Nq - row0) * kVRow);
+#pragma unroll
+        for (int i = 0; i < kDqBlockLoads; ++i) {
+            const uint32_t m0 =
+                __builtin_amdgcn_readfirstlane(smem_base + (uint32_t)(16 * (256 * i + 64 * wave_u)));
+            load_lds(m0, (feed.offy ^ (16 * ((2 * i + (wave_u >> 1)) & 3))) + i * 8 * kVRow, rd);
+        }
+    }
+    // The key tiles are swept twice, as one sequence of 2 nkt ring entries:
+    // entry g is key tile g mod nkt, in ring stage g mod 3.  Entries past the
+    // sequence load zeros (a fixed count per iteration for the waits).
+    auto issue = [&](int g, int st) {
+        const int kt = g < nkt ? g : g - nkt;
+        feed.issue(smem_base + (uint32_t)(kDqBlock + st * kStage), wave_u, gk1, gk2, gv,
+                   (int64_t)kt * 32, g < 2 * nkt ? (int64_t)a.Nk : 0);
+    };
+    issue(0, 0);
+    issue(1, 1);
+    int st = 0, g = 0;  // ring stage and sequence index of the next entry
+    // waits for entry g, refills the stage entry g - 1 used, returns entry g's
+    // stage base
+    auto next = [&]() {
+        wait_loads<kTileLoads>();
+        __syncthreads();
+        issue(g + 2, st == 0 ? 2 : st - 1);
+        const int sb = kDqBlock + st * kStage;
+        st = st == 2 ? 0 : st + 1;
+        ++g;
+        return sb;
+    };
+    const int kr = swap23(l32);
+    const int yk = row_base<kKRow>(kr, lh), yv = row_base<kVRow>(kr, lh);
+    const int yc = col_base<kKRow>(lane);
+    // B operand dD^T: row 32 w + l32 of the block, elements 16 c + 8 lh
+    const int yd = row_base<kVRow>(32 * wave_u + l32, lh);
+
+    // S_k^T = K_k Q_k^T and dP^T = V dD^T of the entry in stage sb (K1 | K2 | V)
+    auto scores = [&](int sb, f32x16& s1, f32x16& s2, f32x16& dp) {
+        const int ykt = opaque(yk | sb), yvt = opaque(yv | sb), ydt = opaque(yd);
+        s1 = s2 = dp = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < kNKB; ++kb) {
+            s1 = mfma(lds_row<0>(smem, ykt ^ (32 * kb)), q1f[kb], s1);
+            s2 = mfma(lds_row<kKTile>(smem, ykt ^ (32 * kb)), q2f[kb], s2);
+        }
+#pragma unroll
+        for (int c = 0; c < kNVB; ++c)
+            dp = mfma(lds_row<2 * kKTile>(smem, yvt ^ (32 * c)), lds_row<0>(smem, ydt ^ (32 * c)), dp);
+    };
+    // A_k of register r (key kt 32 + 8 lh + 16 (r / 8) + r % 8), masked to 0
+    // where that key is not visible (offset from the lane's first key >= lim)
+    auto prob = [&](const f32x16& s, float lse, int r, int lim, auto masked) {
+        float e = fmaf(s[r], sl2, -lse);
+        if constexpr (decltype(masked)::value) {
+            asm volatile("" : "+v"(e));
+            e = 16 * (r >> 3) + (r & 7) < lim ? e : -INFINITY;
+        }
+        return __builtin_amdgcn_exp2f(e);
+    };
+    auto is_full = [&](int kt) {
+        return qw0 + 31 < a.Nq && kt * 32 + 31 < a.Nk && (!CAUSAL || kt * 32 + 31 <= qw0);
+    };
+
+    // ---- sweep 1: delta_k = rowsum(A_k * dP), from the same products as
+    // sweep 2's dP, so that dP - delta_k is formed exactly there.  (dQ as
+    // tau (X_k - delta_k Y_k) in one sweep, X_k = K^T (A_k * dP) and
+    // Y_k = K^T A_k, loses it: when A_k is nearly one-hot, delta_k is nearly
+    // the dominant key's dP and X_k and delta_k Y_k are large and nearly
+    // equal, so the bf16 rounding of their factors survives the difference.)
+    // Tiles kt >= nkt_w mask every key for this wave: it only keeps the ring
+    // going there (loops of their own, so that the compute loops have one
+    // path).
+    for (int kt = 0; kt < nkt_w; ++kt) {
+        const int sb = next();
+        f32x16 s1, s2, dp;
+        scores(sb, s1, s2, dp);
+        const int lim = key_end - kt * 32 - 8 * lh;
+        auto sums = [&](auto masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dsum1 = fmaf(prob(s1, lse1, r, lim, masked), dp[r], dsum1);
+                dsum2 = fmaf(prob(s2, lse2, r, lim, masked), dp[r], dsum2);
+            }
+        };
+        if (is_full(kt))
+            sums(std::false_type{});
+        else
+            sums(std::true_type{});
+    }
+    for (int kt = nkt_w; kt < nkt; ++kt) next();
+    const float delta1 = dsum1 + __shfl_xor(dsum1, 32);
+    const float delta2 = dsum2 + __shfl_xor(dsum2, 32);
+
+    // ---- sweep 2: dQ_k^T += K_k^T dS_k^T with dS_k = A_k (dP - delta_k)
+    // (the factor -lambda of map 2 and tau are applied at the end)
+    for (int kt = 0; kt < nkt_w; ++kt) {
+        const int sb = next();
+        f32x16 s1, s2, dp;
+        scores(sb, s1, s2, dp);
+        const int lim = key_end - kt * 32 - 8 * lh;
+        bf16x8 pg1[2], pg2[2];
+        // (each path packs its own operands: the paths then merge 8 packed
+        // registers rather than 32 floats)
+        auto grads = [&](auto masked) {
+            float g1[16], g2[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                g1[r] = prob(s1, lse1, r, lim, masked) * (dp[r] - delta1);
+                g2[r] = prob(s2, lse2, r, lim, masked) * (dp[r] - delta2);
+            }
+            pack(g1, pg1);
+            pack(g2, pg2);
+        };
+        if (is_full(kt))
+            grads(std::false_type{});
+        else
+            grads(std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        const int yct = opaque(yc | sb);
+#pragma unroll
+        for (int cb = 0; cb < kNCB; ++cb) {
+            const int a0 = yct ^ (64 * cb);
+            mfma_acc(dq1[cb], lds_col<kKRow, 0>(smem, a0), pg1[0]);
+            mfma_acc(dq1[cb], lds_col<kKRow, 16 * kKRow>(smem, a0), pg1[1]);
+            mfma_acc(dq2[cb], lds_col<kKRow, kKTile>(smem, a0), pg2[0]);
+            mfma_acc(dq2[cb], lds_col<kKRow, kKTile + 16 * kKRow>(smem, a0), pg2[1]);
+        }
+    }
+    for (int kt = nkt_w; kt < nkt; ++kt) next();
+    wait_loads<0>();  // the zero-filling loads past the end land before exit
+    settle_wait();
+    settle(dq1);
+    settle(dq2);
+
+    if (!qok) return;
+    const float tau = 1.f / sqrtf((float)kD);
+    const float sc2 = -a.lam[h] * tau;
+    __bf16* o1 = (__bf16*)a.dq1 + ((size_t)bh * a.Nq + qrow) * kD;
+    __bf16* o2 = (__bf16*)a.dq2 + ((size_t)bh * a.Nq + qrow) * kD;
+#pragma unroll
+    for (int cb = 0; cb < kNCB; ++cb) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            bf16x4 v1, v2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v1[e] = (__bf16)(tau * dq1[cb][4 * gq + e]);
+                v2[e] = (__bf16)(sc2 * dq2[cb][4 * gq + e]);
+            }
+            *(bf16x4*)(o1 + 32 * cb + 8 * gq + 4 * lh) = v1;
+            *(bf16x4*)(o2 + 32 * cb + 8 * gq + 4 * lh) = v2;
+        }
+    }
+    if (lh == 0) {
+        a.delta[(size_t)bh * a.Nq + qrow] = delta1;
+        a.delta[((size_t)BH + bh) * a.Nq + qrow] = delta2;
+        *(float4*)(a.rows + 4 * ((size_t)bh * a.Nq + qrow)) = make_float4(lse1, lse2, delta1, delta2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK_1, dK_2, dV
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_ring_kernel(BackwardArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (kStage + kRowStage)];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int BH = a.B * a.H;
+    // key tile kt = blockIdx / BH: under the causal mask the first key tiles
+    // see the most queries, so the longest workgroups start first
+    const int kt = blockIdx.x / BH;
+    const int bh = blockIdx.x - kt * BH;
+    const int h = bh % a.H;
+    const int kw0 = __builtin_amdgcn_readfirstlane(kt * kRowsWG + 32 * wave_u);
+    const int key = kw0 + l32;
+    const bool kok = key < a.Nk;
+
+    const uint8_t* gk1 = (const uint8_t*)a.k1 + (size_t)bh * a.Nk * kKRow;
+    const uint8_t* gk2 = (const uint8_t*)a.k2 + (size_t)bh * a.Nk * kKRow;
+    const uint8_t* gv = (const uint8_t*)a.v + (size_t)bh * a.Nk * kVRow;
+    const uint8_t* gq1 = (const uint8_t*)a.q1 + (size_t)bh * a.Nq * kKRow;
+    const uint8_t* gq2 = (const uint8_t*)a.q2 + (size_t)bh * a.Nq * kKRow;
+    const uint8_t* gdd = (const uint8_t*)a.dd + (size_t)bh * a.Nq * kVRow;
+    const uint8_t* grows = (const uint8_t*)a.rows + (size_t)bh * a.Nq * 16;
+
+    // B operands of this lane's key (column l32): K_k^T over d, V^T over dv
+    bf16x8 k1f[kNKB], k2f[kNKB], vf[kNVB];
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb) {
+        const size_t o = (size_t)key * kKRow + 2 * (16 * kb + 8 * lh);
+        k1f[kb] = kok ? *(const bf16x8*)(gk1 + o) : bf16x8{};
+        k2f[kb] = kok ? *(const bf16x8*)(gk2 + o) : bf16x8{};
+    }
+#pragma unroll
+    for (int c = 0; c < kNVB; ++c)
+        vf[c] = kok ? *(const bf16x8*)(gv + (size_t)key * kVRow + 2 * (16 * c + 8 * lh))
+                    : bf16x8{};
+    const float sl2 = a.scale_log2;
+    const float lam = a.lam[h];
+    // waited for here, before the ring starts (see the dQ kernel)
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb) asm volatile("" ::"v"(k1f[kb]), "v"(k2f[kb]));
+#pragma unroll
+    for (int c = 0; c < kNVB; ++c) asm volatile("" ::"v"(vf[c]));
+    // queries that see this lane's key: q_begin .. q_end - 1
+    const int q_begin = CAUSAL ? key : 0;
+    const int q_end = kok ? a.Nq : q_begin;
+
+    f32x16 dvt[kNDB], dk1t[kNCB], dk2t[kNCB];
+#pragma unroll
+    for (int i = 0; i < kNDB; ++i) dvt[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < kNCB; ++i) dk1t[i] = dk2t[i] = f32x16{};
+
+    const int nqt = (a.Nq + 31) / 32;
+    const int qt0 = CAUSAL ? (kt * kRowsWG) / 32 : 0;
+    // first query tile that sees a key of this wave
+    const int qt_w = CAUSAL ? kw0 / 32 : 0;
+    const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+    TileFeed feed;
+    feed.init(wave_u, lane);
+    // row terms of the tile's 32 queries: each wave loads its own copy (lanes
+    // 32..63 repeat lanes 0..31), so every wave issues the same number of loads
+    const int row_off = 16 * l32;
+    auto issue = [&](int qt) {
+        const uint32_t sti = (uint32_t)(qt & (kStages - 1));
+        const int64_t n = qt < nqt ? (int64_t)a.Nq : 0;
+        feed.issue(smem_base + sti * kStage, wave_u, gq1, gq2, gdd, (int64_t)qt * 32, n);
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+            smem_base + kStages * kStage + sti * kRowStage + (uint32_t)(kRowSlot * wave_u));
+        load_lds(m0, row_off, sgpr_rsrc(grows + (int64_t)qt * 32 * 16, (n - (int64_t)qt * 32) * 16));
+    };
+    issue(qt0);
+    issue(qt0 + 1);
+    issue(qt0 + 2);
+    const int qr = swap23(l32);
+    const int yq = row_base<kKRow>(qr, lh), yd = row_base<kVRow>(qr, lh);
+    const int ycq = col_base<kKRow>(lane), ycd = col_base<kVRow>(lane);
+
+    // tiles qt < qt_w mask every query for this wave: it only keeps the ring
+    // going there (a loop of its own, so that the compute loop has one path)
+    const int qt_c = min(qt_w, nqt);
+    for (int qt = qt0; qt < qt_c; ++qt) {
+        wait_loads<2 * (kTileLoads + 1)>();
+        __syncthreads();
+        issue(qt + 3);
+    }
+    for (int qt = qt_c; qt < nqt; ++qt) {
+        wait_loads<2 * (kTileLoads + 1)>();
+        __syncthreads();  // tile qt is in; stage (qt - 1) mod 4 is free
+        issue(qt + 3);
+        // stage layout Q1 | Q2 | dD; the row terms in a ring of their own
+        const int sb = (qt & (kStages - 1)) * kStage;
+        const int yqt = opaque(yq | sb), ydt = opaque(yd | sb);
+        const int ycqt = opaque(ycq | sb), ycdt = opaque(ycd | sb);
+        const float4* srow = (const float4*)(smem + kStages * kStage +
+                                             (qt & (kStages - 1)) * kRowStage + kRowSlot * wave_u);
+        f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < kNKB; ++kb) {
+            s1 = mfma(lds_row<0>(smem, yqt ^ (32 * kb)), k1f[kb], s1);
+            s2 = mfma(lds_row<kKTile>(smem, yqt ^ (32 * kb)), k2f[kb], s2);
+        }
+#pragma unroll
+        for (int c = 0; c < kNVB; ++c) dp = mfma(lds_row<2 * kKTile>(smem, ydt ^ (32 * c)), vf[c], dp);
+
+        bf16x8 pwd[2], pd1[2], pd2[2];
+        const bool full = kw0 + 31 < a.Nk && qt * 32 + 31 < a.Nq && (!CAUSAL || kw0 + 31 <= qt * 32);
+        // register r holds query qt 32 + 8 lh + (16 (r / 8) + r % 8), visible
+        // while that offset minus lo is below span (unsigned)
+        const int lo = q_begin - qt * 32 - 8 * lh;
+        const unsigned span = (unsigned)(q_end - q_begin);
+        auto probs = [&](auto masked) {
+            float wd[16], d1[16], d2[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
+                const float4 tr = srow[qi];
+                float e1 = fmaf(s1[r], sl2, -tr.x), e2 = fmaf(s2[r], sl2, -tr.y);
+                if constexpr (decltype(masked)::value) {
+                    const bool ok = (unsigned)(16 * (r >> 3) + (r & 7) - lo) < span;
+                    asm volatile("" : "+v"(e1), "+v"(e2));
+                    e1 = ok ? e1 : -INFINITY;
+                    e2 = ok ? e2 : -INFINITY;
+                }
+                const float p1 = __builtin_amdgcn_exp2f(e1);
+                const float p2 = __builtin_amdgcn_exp2f(e2);
+                wd[r] = p1 - lam * p2;
+                d1[r] = p1 * (dp[r] - tr.z);
+                d2[r] = -lam * p2 * (dp[r] - tr.w);
+            }
+            pack(wd, pwd);
+            pack(d1, pd1);
+            pack(d2, pd2);
+        };
+        if (full)
+            probs(std::false_type{});
+        else
+            probs(std::true_type{});
+        // dV^T += dD^T W,  dK_k^T += Q_k^T dS_k  (k = queries)
+#pragma unroll
+        for (int db = 0; db < kNDB; ++db) {
+            const int a0 = ycdt ^ (64 * db);
+            mfma_acc(dvt[db], lds_col<kVRow, 2 * kKTile>(smem, a0), pwd[0]);
+            mfma_acc(dvt[db], lds_col<kVRow, 2 * kKTile + 16 * kVRow>(smem, a0), pwd[1]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < kNCB; ++cb) {
+            const int a0 = ycqt ^ (64 * cb);
+            mfma_acc(dk1t[cb], lds_col<kKRow, 0>(smem, a0), pd1[0]);
+            mfma_acc(dk1t[cb], lds_col<kKRow, 16 * kKRow>(smem, a0), pd1[1]);
+            mfma_acc(dk2t[cb], lds_col<kKRow, kKTile>(smem, a0), pd2[0]);
+            mfma_acc(dk2t[cb], lds_col<kKRow, kKTile + 16 * kKRow>(smem, a0), pd2[1]);
+        }
+    }
+    wait_loads<0>();  // the zero-filling loads past the end land before exit
+    settle_wait();
+    settle(dvt);
+    settle(dk1t);
+    settle(dk2t);
+
+    if (!kok) return;
+    const float tau = 1.f / sqrtf((float)kD);
+    __bf16* o1 = (__bf16*)a.dk1 + ((size_t)bh * a.Nk + key) * kD;
+    __bf16* o2 = (__bf16*)a.dk2 + ((size_t)bh * a.Nk + key) * kD;
+    __bf16* ov = (__bf16*)a.dv + ((size_t)bh * a.Nk + key) * kDV;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int cb = 0; cb < kNCB; ++cb) {
+            bf16x4 w1, w2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w1[e] = (__bf16)(tau * dk1t[cb][4 * g + e]);
+                w2[e] = (__bf16)(tau * dk2t[cb][4 * g + e]);
+            }
+            *(bf16x4*)(o1 + 32 * cb + 8 * g + 4 * lh) = w1;
+            *(bf16x4*)(o2 + 32 * cb + 8 * g + 4 * lh) = w2;
+        }
+#pragma unroll
+        for (int db = 0; db < kNDB; ++db) {
+            bf16x4 wv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[e] = (__bf16)dvt[db][4 * g + e];
+            *(bf16x4*)(ov + 32 * db + 8 * g + 4 * lh) = wv;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward_ring(const BackwardArgs& a, bool causal, hipStream_t stream) {
+    BackwardArgs copy = a;
+    void* args[] = {&copy};
+    const int64_t BH = (int64_t)a.B * a.H;
+    const int64_t g_dq = (int64_t)((a.Nq + kRowsWG - 1) / kRowsWG) * BH;
+    const int64_t g_kv = (int64_t)((a.Nk + kRowsWG - 1) / kRowsWG) * BH;
+    if (g_dq > 0x7fffffff || g_kv > 0x7fffffff) return hipErrorInvalidValue;
+    hipError_t e = hipLaunchKernel(causal ? (const void*)bwd_dq_ring_kernel<true>
+                                          : (const void*)bwd_dq_ring_kernel<false>,
+                                   dim3((unsigned)g_dq), dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel(causal ? (const void*)bwd_dkdv_ring_kernel<true>
+                                  : (const void*)bwd_dkdv_ring_kernel<false>,
+                           dim3((unsigned)g_kv), dim3(kBwdThreads), args, 0, stream);
+}
+
+}  // namespace diffattn

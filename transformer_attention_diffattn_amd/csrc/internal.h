@@ -65,6 +65,7 @@ struct BackwardArgs {
     float* dlam;         // [H]
     void* dd;            // workspace: dD [B][H][Nq][dv] bf16
     float* delta;        // workspace: [2][B][H][Nq] row terms sum_j P_k dP
+    float* rows;         // workspace: [B][H][Nq][4] lse_1, lse_2 (log2 units), delta_1, delta_2
     int32_t B, H, Nq, Nk;
     float lambda_init;
     float eps;
@@ -120,6 +121,9 @@ hipError_t launch_qkv_proj_bf16(const ProjArgs& a, hipStream_t stream);
 // fp8qk: scores from e4m3 queries and keys
 hipError_t launch_prefill_twopass(const PrefillArgs& a, int d, int dv, bool causal, bool fp8qk,
                                   hipStream_t stream);
+// dQ and dK/dV kernels of the head_dim-128, v_dim-256 backward (after the dD
+// prep, before the dlambda sum)
+hipError_t launch_backward_ring(const BackwardArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);
