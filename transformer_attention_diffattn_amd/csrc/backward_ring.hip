@@ -65,9 +65,7 @@ constexpr int kStages = 4;
 constexpr int kRowsWG = 128;        // rows (dq) or keys (dkdv) of a workgroup
 constexpr int kTileLoads = (2 * kKTile + kVTile) / (16 * kBwdThreads);  // per wave and tile
 constexpr int kStage = 2 * kKTile + kVTile;  // 32 KB: X1 | X2 | Y tiles
-constexpr int kDqBlock = kRowsWG * kVRow;     // 64 KB: dD of the dQ workgroup's rows
-constexpr int kDqBlockLoads = kDqBlock / (16 * kBwdThreads);
-constexpr int kDqStages = 3;                 // dQ ring (the dD block takes the rest)
+
 constexpr int kRowSlot = 1024;      // a wave's copy of a tile's row terms (dK/dV)
 constexpr int kRowStage = 4 * kRowSlot;
 static_assert(kStage == 32 * 1024, "stage bases must leave the in-tile address bits free");
@@ -159,20 +157,40 @@ __device__ __forceinline__ void load_lds(uint32_t m0, int voff, i32x4 rsrc) {
 // to cover, since the compiler does not look into the statement: an operand
 // written by a vector instruction needs 2 wait states before the product
 // reads it (the leading s_nop 1), and the accumulators are read back only
-// after settle().  Volatile keeps the products in program order.
+// after settle().  Not volatile: the data dependencies order the products
+// of one accumulator, and the scheduler may move LDS reads and vector work
+// across them.
 __device__ __forceinline__ void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// After the last mfma_acc: the products' latency (at most 16 passes) passes
-// before any accumulator is read by another instruction.
+// After the last mfma_acc: each accumulator passes through a statement that
+// waits out the products' latency (at most 16 passes) before any other
+// instruction reads it; taking the accumulator as an operand orders it after
+// that accumulator's last product.
 template <int N>
 __device__ __forceinline__ void settle(f32x16 (&acc)[N]) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+    for (int i = 0; i < N; ++i) asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+a"(acc[i]));
 }
-__device__ __forceinline__ void settle_wait() {
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+
+// Work item of workgroup w in a grid of n tiles per (batch, head) times BH:
+// sets the tile rank t (0 = the longest causal tile) and bh.  Workgroups are
+// dispatched round-robin over the 8 XCDs (w runs on XCD w mod 8), each with
+// its own L2.  When BH is a multiple of 8, XCD x takes the heads
+// bh = x mod 8 one after the other (the grid's w / 8-th item of that XCD is
+// tile (w / 8) mod n of its (w / 8) / n-th head): the XCD's compute units
+// sweep the same head's tiles at the same time, and each tile they share comes
+// from HBM into that L2 about once.  Else tile-major over all heads.
+__device__ __forceinline__ void xcd_item(int w, int n, int BH, int& t, int& bh) {
+    if ((BH & 7) == 0) {
+        const int i = w >> 3, hl = i / n;
+        t = i - hl * n;
+        bh = 8 * hl + (w & 7);
+    } else {
+        t = w / BH;
+        bh = w - t * BH;
+    }
 }
 
 template <int N>
@@ -225,83 +243,122 @@ struct TileFeed {
 // ---------------------------------------------------------------------------
 // dQ_1, dQ_2, delta_1, delta_2 and the row terms
 // ---------------------------------------------------------------------------
+constexpr int kDqThreads = 512;  // 8 waves: 4 query blocks x 2 maps, two per SIMD
+constexpr int kDqStages = 3;
+constexpr int kDqLoads = kStage / (16 * kDqThreads);  // per wave and tile
+constexpr int kXSlot = 64 * 16 * 4;                   // a wave's 16 floats per lane
+constexpr int kDqSmem = kDqStages * kStage + 8 * kXSlot;
+static_assert(kDqLoads * 16 * kDqThreads == kStage, "whole loads per wave");
+
+// One tile (K1 | K2 | V, 32 rows each) into a ring stage with 8 waves: load
+// instruction i of wave w fills chunk positions 512 i + 64 w .. + 63 (i = 0:
+// K1, 1: K2, 2 and 3: V), each lane fetching the chunk the swizzle puts at
+// its position.
+struct TileFeed8 {
+    int off[kDqLoads];
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < kDqLoads; ++i) {
+            const int p = 512 * i + 64 * wave + lane;
+            if (p < 1024) {
+                const int q = p & 511, row = q >> 4;
+                off[i] = row * kKRow + 16 * ((q & 15) ^ rswz(row));
+            } else {
+                const int q = p - 1024, row = q >> 5;
+                off[i] = row * kVRow + 16 * ((q & 31) ^ rswz(row));
+            }
+        }
+    }
+    __device__ __forceinline__ void issue(uint32_t stage, int wave, const uint8_t* k1,
+                                          const uint8_t* k2, const uint8_t* v, int64_t row0,
+                                          int64_t n) const {
+        const int64_t left = n - row0;
+        const i32x4 r1 = sgpr_rsrc(k1 + row0 * kKRow, left * kKRow);
+        const i32x4 r2 = sgpr_rsrc(k2 + row0 * kKRow, left * kKRow);
+        const i32x4 rv = sgpr_rsrc(v + row0 * kVRow, left * kVRow);
+#pragma unroll
+        for (int i = 0; i < kDqLoads; ++i) {
+            const uint32_t m0 =
+                __builtin_amdgcn_readfirstlane(stage + (uint32_t)(16 * (512 * i + 64 * wave)));
+            load_lds(m0, off[i], i == 0 ? r1 : (i == 1 ? r2 : rv));
+        }
+    }
+};
+
+// Workgroup = 128 query rows of one (batch, head); wave w owns rows
+// 32 (w mod 4) .. and map w / 4.  Two sweeps over the key tiles (delta first,
+// then dQ; see the file comment).  Per tile each wave forms its map's scores
+// S^T = K Q^T (8 products) and dP^T over its map's half of the dv channels
+// (8 products), and the two waves of a query block add their halves through
+// LDS: both compute own + partner, and fp32 addition commutes, so they hold
+// the same dP.  Sweep 2 adds dQ^T += K^T dS^T (8 products).
 template <bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dq_ring_kernel(BackwardArgs a) {
-    // dD of the workgroup's 128 rows (64 KB), then a 3-stage ring of K1 | K2 | V
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kDqBlock + kDqStages * kStage];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kDqSmem];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int l32 = lane & 31, lh = lane >> 5;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int qb = wave & 3, map = wave >> 2;
     const int BH = a.B * a.H;
     const int nqt = (a.Nq + kRowsWG - 1) / kRowsWG;
-    const int t = blockIdx.x / BH;  // longest causal tiles first
-    const int bh = blockIdx.x - t * BH;
+    int t, bh;  // longest causal tiles first
+    xcd_item(blockIdx.x, nqt, BH, t, bh);
     const int qt = CAUSAL ? nqt - 1 - t : t;
     const int h = bh % a.H;
-    const int qw0 = __builtin_amdgcn_readfirstlane(qt * kRowsWG + 32 * wave_u);
+    const int qw0 = qt * kRowsWG + 32 * qb;
     const int qrow = qw0 + l32;
     const bool qok = qrow < a.Nq;
 
-    const uint8_t* gq1 = (const uint8_t*)a.q1 + (size_t)bh * a.Nq * kKRow;
-    const uint8_t* gq2 = (const uint8_t*)a.q2 + (size_t)bh * a.Nq * kKRow;
+    const uint8_t* gq = (const uint8_t*)(map ? a.q2 : a.q1) + (size_t)bh * a.Nq * kKRow;
     const uint8_t* gk1 = (const uint8_t*)a.k1 + (size_t)bh * a.Nk * kKRow;
     const uint8_t* gk2 = (const uint8_t*)a.k2 + (size_t)bh * a.Nk * kKRow;
     const uint8_t* gv = (const uint8_t*)a.v + (size_t)bh * a.Nk * kVRow;
     const uint8_t* gdd = (const uint8_t*)a.dd + (size_t)bh * a.Nq * kVRow;
 
-    // B operands of this lane's query (column l32): Q_k^T over d (dD^T over
-    // dv is read from the LDS block each tile)
-    bf16x8 q1f[kNKB], q2f[kNKB];
+    // B operands of this lane's query (column l32): Q^T of the wave's map over
+    // d, dD^T over the map's half of dv (channels 128 map ..)
+    bf16x8 qf[kNKB], df[kNVB / 2];
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb) {
-        const size_t o = (size_t)qrow * kKRow + 2 * (16 * kb + 8 * lh);
-        q1f[kb] = qok ? *(const bf16x8*)(gq1 + o) : bf16x8{};
-        q2f[kb] = qok ? *(const bf16x8*)(gq2 + o) : bf16x8{};
-    }
+    for (int kb = 0; kb < kNKB; ++kb)
+        qf[kb] = qok ? *(const bf16x8*)(gq + (size_t)qrow * kKRow + 2 * (16 * kb + 8 * lh))
+                     : bf16x8{};
+#pragma unroll
+    for (int c = 0; c < kNVB / 2; ++c)
+        df[c] = qok ? *(const bf16x8*)(gdd + (size_t)qrow * kVRow +
+                                       2 * (kDV / 2 * map + 16 * c + 8 * lh))
+                    : bf16x8{};
     // keys visible to this lane's query: 0 .. key_end - 1
     const int key_end = qok ? (CAUSAL ? min(a.Nk, qrow + 1) : a.Nk) : 0;
-    const float lse1 = qok ? a.lse[(size_t)bh * a.Nq + qrow] * kLog2e : 0.f;
-    const float lse2 = qok ? a.lse[((size_t)BH + bh) * a.Nq + qrow] * kLog2e : 0.f;
+    const float lse = qok ? a.lse[((size_t)map * BH + bh) * a.Nq + qrow] * kLog2e : 0.f;
     const float sl2 = a.scale_log2;
     // The compiler counts only its own loads when it waits for these, so a
     // first use inside the loop would wait for the ring's loads as well (on
     // every tile).  Used here, before the ring starts, they are complete.
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb) asm volatile("" ::"v"(q1f[kb]), "v"(q2f[kb]));
-    asm volatile("" ::"v"(lse1), "v"(lse2));
-
-    f32x16 dq1[kNCB], dq2[kNCB];
+    for (int kb = 0; kb < kNKB; ++kb) asm volatile("" ::"v"(qf[kb]));
 #pragma unroll
-    for (int cb = 0; cb < kNCB; ++cb) dq1[cb] = dq2[cb] = f32x16{};
-    float dsum1 = 0.f, dsum2 = 0.f;
+    for (int c = 0; c < kNVB / 2; ++c) asm volatile("" ::"v"(df[c]));
+    asm volatile("" ::"v"(lse));
+
+    f32x16 dq[kNCB];
+#pragma unroll
+    for (int cb = 0; cb < kNCB; ++cb) dq[cb] = f32x16{};
+    float dsum = 0.f;
 
     const int nkt_all = (a.Nk + 31) / 32;
     const int nkt = CAUSAL ? min(nkt_all, (qt * kRowsWG + kRowsWG + 31) / 32) : nkt_all;
-    // key tiles in which some key is visible to some row of this wave
+    // key tiles in which some key is visible to some row of this query block
     const int nkt_w = CAUSAL ? min(nkt, (qw0 + 31) / 32 + 1) : nkt;
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-    TileFeed feed;
-    feed.init(wave_u, lane);
-    {
-        // the dD block: 16 loads per wave, row 8 i + 2 w + lane / 32 in
-        // instruction i (the Y part of the tile feed, continued)
-        const int64_t row0 = (int64_t)qt * kRowsWG;
-        const i32x4 rd = sgpr_rsrc(gdd + row0 * kVRow, ((int64_t)a.Nq - row0) * kVRow);
-#pragma unroll
-        for (int i = 0; i < kDqBlockLoads; ++i) {
-            const uint32_t m0 =
-                __builtin_amdgcn_readfirstlane(smem_base + (uint32_t)(16 * (256 * i + 64 * wave_u)));
-            load_lds(m0, (feed.offy ^ (16 * ((2 * i + (wave_u >> 1)) & 3))) + i * 8 * kVRow, rd);
-        }
-    }
+    TileFeed8 feed;
+    feed.init(wave, lane);
     // The key tiles are swept twice, as one sequence of 2 nkt ring entries:
     // entry g is key tile g mod nkt, in ring stage g mod 3.  Entries past the
     // sequence load zeros (a fixed count per iteration for the waits).
     auto issue = [&](int g, int st) {
         const int kt = g < nkt ? g : g - nkt;
-        feed.issue(smem_base + (uint32_t)(kDqBlock + st * kStage), wave_u, gk1, gk2, gv,
-                   (int64_t)kt * 32, g < 2 * nkt ? (int64_t)a.Nk : 0);
+        feed.issue(smem_base + (uint32_t)(st * kStage), wave, gk1, gk2, gv, (int64_t)kt * 32,
+                   g < 2 * nkt ? (int64_t)a.Nk : 0);
     };
     issue(0, 0);
     issue(1, 1);
@@ -309,141 +366,141 @@ void bwd_dq_ring_kernel(BackwardArgs a) {
     // waits for entry g, refills the stage entry g - 1 used, returns entry g's
     // stage base
     auto next = [&]() {
-        wait_loads<kTileLoads>();
+        wait_loads<kDqLoads>();
         __syncthreads();
         issue(g + 2, st == 0 ? 2 : st - 1);
-        const int sb = kDqBlock + st * kStage;
+        const int sb = st * kStage;
         st = st == 2 ? 0 : st + 1;
         ++g;
         return sb;
     };
     const int kr = swap23(l32);
-    const int yk = row_base<kKRow>(kr, lh), yv = row_base<kVRow>(kr, lh);
-    const int yc = col_base<kKRow>(lane);
-    // B operand dD^T: row 32 w + l32 of the block, elements 16 c + 8 lh
-    const int yd = row_base<kVRow>(32 * wave_u + l32, lh);
+    // the wave's map selects the K tile (bit 13: K2 is 8 KB on) and the half
+    // of each V row (bit 8: its second 256 bytes)
+    const int yk = row_base<kKRow>(kr, lh) | (map << 13);
+    const int yv = row_base<kVRow>(kr, lh) | (map << 8);
+    const int yc = col_base<kKRow>(lane) | (map << 13);
+    const int x_own = kDqStages * kStage + kXSlot * wave;
+    const int x_oth = kDqStages * kStage + kXSlot * (wave ^ 4);
 
-    // S_k^T = K_k Q_k^T and dP^T = V dD^T of the entry in stage sb (K1 | K2 | V)
-    auto scores = [&](int sb, f32x16& s1, f32x16& s2, f32x16& dp) {
-        const int ykt = opaque(yk | sb), yvt = opaque(yv | sb), ydt = opaque(yd);
-        s1 = s2 = dp = f32x16{};
+    // S^T = K Q^T and this map's half of dP^T = V dD^T, entry in stage sb
+    auto scores = [&](int sb, f32x16& s, f32x16& dph) {
+        const int ykt = opaque(yk | sb), yvt = opaque(yv | sb);
+        s = dph = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb) {
-            s1 = mfma(lds_row<0>(smem, ykt ^ (32 * kb)), q1f[kb], s1);
-            s2 = mfma(lds_row<kKTile>(smem, ykt ^ (32 * kb)), q2f[kb], s2);
-        }
+        for (int kb = 0; kb < kNKB; ++kb) s = mfma(lds_row<0>(smem, ykt ^ (32 * kb)), qf[kb], s);
 #pragma unroll
-        for (int c = 0; c < kNVB; ++c)
-            dp = mfma(lds_row<2 * kKTile>(smem, yvt ^ (32 * c)), lds_row<0>(smem, ydt ^ (32 * c)), dp);
+        for (int c = 0; c < kNVB / 2; ++c)
+            dph = mfma(lds_row<2 * kKTile>(smem, yvt ^ (32 * c)), df[c], dph);
     };
-    // A_k of register r (key kt 32 + 8 lh + 16 (r / 8) + r % 8), masked to 0
-    // where that key is not visible (offset from the lane's first key >= lim)
-    auto prob = [&](const f32x16& s, float lse, int r, int lim, auto masked) {
-        float e = fmaf(s[r], sl2, -lse);
-        if constexpr (decltype(masked)::value) {
-            asm volatile("" : "+v"(e));
-            e = 16 * (r >> 3) + (r & 7) < lim ? e : -INFINITY;
+    // dP = own half + partner's half (the barrier between writing and reading
+    // is the second of the iteration; the next iteration's first one keeps the
+    // partner's read ahead of this wave's next write)
+    auto exchange = [&](const f32x16& own) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(float4*)(smem + x_own + 1024 * i + 16 * lane) =
+                make_float4(own[4 * i], own[4 * i + 1], own[4 * i + 2], own[4 * i + 3]);
+        __syncthreads();
+        f32x16 dp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 o = *(const float4*)(smem + x_oth + 1024 * i + 16 * lane);
+            dp[4 * i] = own[4 * i] + o.x;
+            dp[4 * i + 1] = own[4 * i + 1] + o.y;
+            dp[4 * i + 2] = own[4 * i + 2] + o.z;
+            dp[4 * i + 3] = own[4 * i + 3] + o.w;
         }
-        return __builtin_amdgcn_exp2f(e);
+        return dp;
     };
-    auto is_full = [&](int kt) {
-        return qw0 + 31 < a.Nq && kt * 32 + 31 < a.Nk && (!CAUSAL || kt * 32 + 31 <= qw0);
-    };
-
-    // ---- sweep 1: delta_k = rowsum(A_k * dP), from the same products as
-    // sweep 2's dP, so that dP - delta_k is formed exactly there.  (dQ as
-    // tau (X_k - delta_k Y_k) in one sweep, X_k = K^T (A_k * dP) and
-    // Y_k = K^T A_k, loses it: when A_k is nearly one-hot, delta_k is nearly
-    // the dominant key's dP and X_k and delta_k Y_k are large and nearly
-    // equal, so the bf16 rounding of their factors survives the difference.)
-    // Tiles kt >= nkt_w mask every key for this wave: it only keeps the ring
-    // going there (loops of their own, so that the compute loops have one
-    // path).
-    for (int kt = 0; kt < nkt_w; ++kt) {
-        const int sb = next();
-        f32x16 s1, s2, dp;
-        scores(sb, s1, s2, dp);
-        const int lim = key_end - kt * 32 - 8 * lh;
-        auto sums = [&](auto masked) {
+    // A of register r (key kt 32 + 8 lh + 16 (r / 8) + r % 8); edge tiles
+    // mask keys at offset >= lim from the lane's first key (min with -inf
+    // rather than a select, formed on every lane)
+    auto probs = [&](const f32x16& s, int kt, float (&p)[16]) {
+        const bool full = qw0 + 31 < a.Nq && kt * 32 + 31 < a.Nk && (!CAUSAL || kt * 32 + 31 <= qw0);
+        if (full) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse));
+        } else {
+            const int lim = key_end - kt * 32 - 8 * lh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                dsum1 = fmaf(prob(s1, lse1, r, lim, masked), dp[r], dsum1);
-                dsum2 = fmaf(prob(s2, lse2, r, lim, masked), dp[r], dsum2);
+                const float cap = 16 * (r >> 3) + (r & 7) < lim ? INFINITY : -INFINITY;
+                p[r] = __builtin_amdgcn_exp2f(fminf(fmaf(s[r], sl2, -lse), cap));
             }
-        };
-        if (is_full(kt))
-            sums(std::false_type{});
-        else
-            sums(std::true_type{});
+        }
+    };
+
+    // ---- sweep 1: delta = rowsum(A * dP), from the same products as sweep
+    // 2's dP, so that dP - delta is formed exactly there.  (dQ as
+    // tau (X - delta Y) in one sweep, X = K^T (A * dP) and Y = K^T A, loses
+    // it: when A is nearly one-hot, delta is nearly the dominant key's dP and
+    // X and delta Y are large and nearly equal, so the bf16 rounding of their
+    // factors survives the difference.)  Tiles kt >= nkt_w mask every key of
+    // the query block: its waves only keep the ring and the barriers going
+    // there (loops of their own, so that the compute loops have one path).
+    for (int kt = 0; kt < nkt_w; ++kt) {
+        const int sb = next();
+        f32x16 s, dph;
+        scores(sb, s, dph);
+        float p[16];
+        probs(s, kt, p);
+        const f32x16 dp = exchange(dph);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsum = fmaf(p[r], dp[r], dsum);
     }
-    for (int kt = nkt_w; kt < nkt; ++kt) next();
-    const float delta1 = dsum1 + __shfl_xor(dsum1, 32);
-    const float delta2 = dsum2 + __shfl_xor(dsum2, 32);
+    for (int kt = nkt_w; kt < nkt; ++kt) {
+        next();
+        __syncthreads();
+    }
+    const float delta = dsum + __shfl_xor(dsum, 32);
 
-    // ---- sweep 2: dQ_k^T += K_k^T dS_k^T with dS_k = A_k (dP - delta_k)
-    // (the factor -lambda of map 2 and tau are applied at the end)
+    // ---- sweep 2: dQ^T += K^T dS^T with dS = A (dP - delta) (the factor
+    // -lambda of map 2 and tau are applied at the end)
     for (int kt = 0; kt < nkt_w; ++kt) {
         const int sb = next();
-        f32x16 s1, s2, dp;
-        scores(sb, s1, s2, dp);
-        const int lim = key_end - kt * 32 - 8 * lh;
-        bf16x8 pg1[2], pg2[2];
-        // (each path packs its own operands: the paths then merge 8 packed
-        // registers rather than 32 floats)
-        auto grads = [&](auto masked) {
-            float g1[16], g2[16];
+        f32x16 s, dph;
+        scores(sb, s, dph);
+        float p[16];
+        probs(s, kt, p);
+        const f32x16 dp = exchange(dph);
+        float gr[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                g1[r] = prob(s1, lse1, r, lim, masked) * (dp[r] - delta1);
-                g2[r] = prob(s2, lse2, r, lim, masked) * (dp[r] - delta2);
-            }
-            pack(g1, pg1);
-            pack(g2, pg2);
-        };
-        if (is_full(kt))
-            grads(std::false_type{});
-        else
-            grads(std::true_type{});
-        __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 16; ++r) gr[r] = p[r] * (dp[r] - delta);
+        bf16x8 pg[2];
+        pack(gr, pg);
         const int yct = opaque(yc | sb);
 #pragma unroll
         for (int cb = 0; cb < kNCB; ++cb) {
             const int a0 = yct ^ (64 * cb);
-            mfma_acc(dq1[cb], lds_col<kKRow, 0>(smem, a0), pg1[0]);
-            mfma_acc(dq1[cb], lds_col<kKRow, 16 * kKRow>(smem, a0), pg1[1]);
-            mfma_acc(dq2[cb], lds_col<kKRow, kKTile>(smem, a0), pg2[0]);
-            mfma_acc(dq2[cb], lds_col<kKRow, kKTile + 16 * kKRow>(smem, a0), pg2[1]);
+            dq[cb] = mfma(lds_col<kKRow, 0>(smem, a0), pg[0], dq[cb]);
+            dq[cb] = mfma(lds_col<kKRow, 16 * kKRow>(smem, a0), pg[1], dq[cb]);
         }
     }
-    for (int kt = nkt_w; kt < nkt; ++kt) next();
+    for (int kt = nkt_w; kt < nkt; ++kt) {
+        next();
+        __syncthreads();
+    }
     wait_loads<0>();  // the zero-filling loads past the end land before exit
-    settle_wait();
-    settle(dq1);
-    settle(dq2);
 
     if (!qok) return;
     const float tau = 1.f / sqrtf((float)kD);
-    const float sc2 = -a.lam[h] * tau;
-    __bf16* o1 = (__bf16*)a.dq1 + ((size_t)bh * a.Nq + qrow) * kD;
-    __bf16* o2 = (__bf16*)a.dq2 + ((size_t)bh * a.Nq + qrow) * kD;
+    const float sc = map ? -a.lam[h] * tau : tau;
+    __bf16* o = (__bf16*)(map ? a.dq2 : a.dq1) + ((size_t)bh * a.Nq + qrow) * kD;
 #pragma unroll
     for (int cb = 0; cb < kNCB; ++cb) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-            bf16x4 v1, v2;
+            bf16x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v1[e] = (__bf16)(tau * dq1[cb][4 * gq + e]);
-                v2[e] = (__bf16)(sc2 * dq2[cb][4 * gq + e]);
-            }
-            *(bf16x4*)(o1 + 32 * cb + 8 * gq + 4 * lh) = v1;
-            *(bf16x4*)(o2 + 32 * cb + 8 * gq + 4 * lh) = v2;
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(sc * dq[cb][4 * gq + e]);
+            *(bf16x4*)(o + 32 * cb + 8 * gq + 4 * lh) = v;
         }
     }
     if (lh == 0) {
-        a.delta[(size_t)bh * a.Nq + qrow] = delta1;
-        a.delta[((size_t)BH + bh) * a.Nq + qrow] = delta2;
-        *(float4*)(a.rows + 4 * ((size_t)bh * a.Nq + qrow)) = make_float4(lse1, lse2, delta1, delta2);
+        a.delta[((size_t)map * BH + bh) * a.Nq + qrow] = delta;
+        // row terms (lse_1, delta_1, lse_2, delta_2): this map's pair
+        *(float2*)(a.rows + 4 * ((size_t)bh * a.Nq + qrow) + 2 * map) = make_float2(lse, delta);
     }
 }
 
@@ -460,8 +517,8 @@ void bwd_dkdv_ring_kernel(BackwardArgs a) {
     const int BH = a.B * a.H;
     // key tile kt = blockIdx / BH: under the causal mask the first key tiles
     // see the most queries, so the longest workgroups start first
-    const int kt = blockIdx.x / BH;
-    const int bh = blockIdx.x - kt * BH;
+    int kt, bh;
+    xcd_item(blockIdx.x, (a.Nk + kRowsWG - 1) / kRowsWG, BH, kt, bh);
     const int h = bh % a.H;
     const int kw0 = __builtin_amdgcn_readfirstlane(kt * kRowsWG + 32 * wave_u);
     const int key = kw0 + l32;
@@ -559,7 +616,9 @@ void bwd_dkdv_ring_kernel(BackwardArgs a) {
         bf16x8 pwd[2], pd1[2], pd2[2];
         const bool full = kw0 + 31 < a.Nk && qt * 32 + 31 < a.Nq && (!CAUSAL || kw0 + 31 <= qt * 32);
         // register r holds query qt 32 + 8 lh + (16 (r / 8) + r % 8), visible
-        // while that offset minus lo is below span (unsigned)
+        // while that offset minus lo is below span (unsigned).  Full tiles skip
+        // the mask; each path packs its own operands (the paths then merge 24
+        // packed registers rather than 48 floats).
         const int lo = q_begin - qt * 32 - 8 * lh;
         const unsigned span = (unsigned)(q_end - q_begin);
         auto probs = [&](auto masked) {
@@ -568,17 +627,19 @@ void bwd_dkdv_ring_kernel(BackwardArgs a) {
             for (int r = 0; r < 16; ++r) {
                 const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
                 const float4 tr = srow[qi];
-                float e1 = fmaf(s1[r], sl2, -tr.x), e2 = fmaf(s2[r], sl2, -tr.y);
+                float e1 = fmaf(s1[r], sl2, -tr.x), e2 = fmaf(s2[r], sl2, -tr.z);
                 if constexpr (decltype(masked)::value) {
-                    const bool ok = (unsigned)(16 * (r >> 3) + (r & 7) - lo) < span;
-                    asm volatile("" : "+v"(e1), "+v"(e2));
-                    e1 = ok ? e1 : -INFINITY;
-                    e2 = ok ? e2 : -INFINITY;
+                    // min with +inf or -inf: formed on every lane (a select lets
+                    // the compiler put the row-term read under a branch)
+                    const float cap =
+                        (unsigned)(16 * (r >> 3) + (r & 7) - lo) < span ? INFINITY : -INFINITY;
+                    e1 = fminf(e1, cap);
+                    e2 = fminf(e2, cap);
                 }
                 const float p1 = __builtin_amdgcn_exp2f(e1);
                 const float p2 = __builtin_amdgcn_exp2f(e2);
                 wd[r] = p1 - lam * p2;
-                d1[r] = p1 * (dp[r] - tr.z);
+                d1[r] = p1 * (dp[r] - tr.y);
                 d2[r] = -lam * p2 * (dp[r] - tr.w);
             }
             pack(wd, pwd);
@@ -606,7 +667,6 @@ void bwd_dkdv_ring_kernel(BackwardArgs a) {
         }
     }
     wait_loads<0>();  // the zero-filling loads past the end land before exit
-    settle_wait();
     settle(dvt);
     settle(dk1t);
     settle(dk2t);
@@ -648,9 +708,9 @@ hipError_t launch_backward_ring(const BackwardArgs& a, bool causal, hipStream_t 
     const int64_t g_dq = (int64_t)((a.Nq + kRowsWG - 1) / kRowsWG) * BH;
     const int64_t g_kv = (int64_t)((a.Nk + kRowsWG - 1) / kRowsWG) * BH;
     if (g_dq > 0x7fffffff || g_kv > 0x7fffffff) return hipErrorInvalidValue;
-    hipError_t e = hipLaunchKernel(causal ? (const void*)bwd_dq_ring_kernel<true>
-                                          : (const void*)bwd_dq_ring_kernel<false>,
-                                   dim3((unsigned)g_dq), dim3(kBwdThreads), args, 0, stream);
+    hipError_t e = hipLaunchKernel(causal ? (const void*)bwd_dq_pair_kernel<true>
+                                          : (const void*)bwd_dq_pair_kernel<false>,
+                                   dim3((unsigned)g_dq), dim3(kDqThreads), args, 0, stream);
     if (e != hipSuccess) return e;
     return hipLaunchKernel(causal ? (const void*)bwd_dkdv_ring_kernel<true>
                                   : (const void*)bwd_dkdv_ring_kernel<false>,
