@@ -9,34 +9,32 @@
 //   dQ_k = tau dS_k K_k,  dK_k = tau dS_k^T Q_k,  dV = (A_1 - lambda A_2)^T dD.
 // A_k = exp(S_k tau - lse_k) from the training forward's log-sum-exp.
 //
-// Why a kernel of its own.  At head_dim 128 a wave that owns 32 rows and both
-// maps holds 128 registers of resident operands (both maps' Q or K columns and
-// dD or V columns) and up to 256 of accumulators (dK/dV: dV over 256
-// channels and both dK_k; dQ: both dQ_k).  That fits one wave per SIMD with
-// its 512 registers (accumulators in the AGPRs), and at this head size a
-// tile carries 48-64 products (1,536-2,048 MFMA cycles) against ~200 vector
-// instructions, so one wave keeps the matrix core fed if its operands arrive
-// in time.  Both maps in one wave also compute dP once for the two.
+// Why kernels of their own.  At head_dim 128 the resident operands of a
+// wave (Q or K columns over d, dD or V columns over dv) and its accumulators
+// outgrow the head_dim-64 kernels' register budget.
 //
-//   dq    workgroup = 128 query rows of one (batch, head), wave w rows
-//         32 w .. 32 w + 31 of both maps; sweeps the key tiles twice.  Per
-//         tile, both sweeps: S_k^T = K_k Q_k^T (2 x 8 products) and
-//         dP^T = V dD^T (16); sweep 1 sums delta_k = rowsum(A_k * dP),
-//         sweep 2 forms dS_k = A_k (dP - delta_k) in fp32 and accumulates
-//         dQ_k^T += K_k^T dS_k^T (2 x 8).  Writes dQ_k, delta_k and the row
-//         terms of the dK/dV kernel.  dD of the workgroup's rows sits in LDS
-//         (64 KB) beside a 3-stage ring.
-//   dkdv  workgroup = 128 keys, wave w keys 32 w .. of both maps; sweeps the
-//         query tiles.  Per tile: S_k = Q_k K_k^T (2 x 8), dP = dD V^T (16),
+//   dq    workgroup = 128 query rows of one (batch, head), 8 waves, wave w
+//         rows 32 (w mod 4) .. of map w / 4, two waves per SIMD.  Sweeps the
+//         key tiles twice.  Per tile, both sweeps: S^T = K Q^T (8 products)
+//         and dP^T over the wave's half of the dv channels (8), the two
+//         halves added through LDS; sweep 1 sums delta = rowsum(A * dP),
+//         sweep 2 forms dS = A (dP - delta) in fp32 and accumulates
+//         dQ^T += K^T dS^T (8).  Writes dQ_k, delta_k and the row terms of
+//         the dK/dV kernel.
+//   dkdv  workgroup = 128 keys, wave w keys 32 w .. of both maps, one wave
+//         per SIMD: 128 registers of resident K1^T, K2^T, V^T and 256 of
+//         accumulators (dV over 256 channels, both dK_k) in the AGPRs.  Per
+//         query tile: S_k = Q_k K_k^T (2 x 8), dP = dD V^T (16),
 //         dV^T += dD^T W with W = A_1 - lambda A_2 (16), dK_k^T += Q_k^T dS_k
 //         (2 x 8).
 //
-// Tiles of 32 rows stream through a 4-stage LDS ring, three tiles ahead, by
-// buffer loads with the LDS destination (no registers, no LDS stores).  Each
+// Tiles of 32 rows stream through a 3- or 4-stage LDS ring, two or three
+// tiles ahead, by buffer loads with the LDS destination (no registers, no
+// LDS stores).  Each
 // tile is read both as rows (16-byte reads: the A operand of the score and
 // dP products, rows in swap23 order so that score accumulators are the next
 // product's B operands) and as columns (ds_read_b64_tr_b16: the transposed
-// A operand of the X, Y, dV and dK products).  One XOR swizzle of a row's
+// A operand of the dQ, dV and dK products).  One XOR swizzle of a row's
 // 16-byte chunks serves both: chunk c of row r sits at position
 // c ^ (4 (r mod 4) + (r / 4) mod 4), which puts the 16 rows of a row read
 // and the 4 rows x 4 chunks of a transposing read on 64 distinct banks.
