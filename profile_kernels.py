@@ -85,6 +85,8 @@ def entries():
         ("qkv_proj_kernel", "causal_prefill_bf16", "proj.hip", "b", ("qkv_proj", "ms_per_call")),
         ("bwd_dq_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
         ("bwd_dkdv_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
+        ("bwd_dq_pair_kernel", "large_head_bf16", "backward_ring.hip+tile_ops.h", "b", None),
+        ("bwd_dkdv_ring_kernel", "large_head_bf16", "backward_ring.hip+tile_ops.h", "b", None),
     ]
 
 
