@@ -74,6 +74,19 @@ static_assert(kKTile % (16 * kBwdThreads) == 0, "a load instruction stays in one
 
 __device__ __forceinline__ int rswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// The swizzle by row length: rows of 256 or 512 bytes use rswz on the low 4
+// bits of the chunk index; 128-byte rows (head_dim 64 tiles of Q and K, two
+// rows per pass over the banks) use c ^ (4 ((r / 2) mod 2) + (r / 4) mod 4),
+// which puts the 16 rows of a row read and the 4 rows x 4 chunks of a
+// transposed read on distinct banks the same way.
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (RB == 128)
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else
+        return rswz(r);
+}
+
 // LDS addressing.  Every tile sits at a fixed offset in its ring stage and a
 // stage's base is a multiple of 32 KB, while a read's address within a tile
 // is below 16 KB, so the address of a read is
@@ -90,7 +103,7 @@ __device__ __forceinline__ int rswz(int r) { return ((r & 3) << 2) | ((r >> 2) &
 // base ^ (32 kb).
 template <int RB>
 __device__ __forceinline__ int row_base(int row, int lh) {
-    return row * RB + 16 * (lh ^ rswz(row));
+    return row * RB + 16 * (lh ^ swz<RB>(row));
 }
 
 // Transposed reads (A operand column cb + l32 over rows k0 + 8 lh .. + 7,
@@ -103,7 +116,8 @@ template <int RB>
 __device__ __forceinline__ int col_base(int lane) {
     const int g = lane >> 4, e = (lane & 15) >> 2, r = lane & 3;
     const int w = 2 * (g & 1) + (r >> 1), z = 2 * (g >> 1);
-    return (8 * (g >> 1) + e) * RB + 64 * e + 16 * (w ^ z) + 8 * (r & 1);
+    // (128-byte rows: the swizzle's bit 2 comes from (row / 2) mod 2 = e / 2)
+    return (8 * (g >> 1) + e) * RB + 64 * (RB == 128 ? e >> 1 : e) + 16 * (w ^ z) + 8 * (r & 1);
 }
 
 __device__ __forceinline__ int opaque(int x) {
@@ -243,27 +257,45 @@ struct TileFeed {
 // ---------------------------------------------------------------------------
 constexpr int kDqThreads = 512;  // 8 waves: 4 query blocks x 2 maps, two per SIMD
 constexpr int kDqStages = 3;
-constexpr int kDqLoads = kStage / (16 * kDqThreads);  // per wave and tile
-constexpr int kXSlot = 64 * 16 * 4;                   // a wave's 16 floats per lane
-constexpr int kDqSmem = kDqStages * kStage + 8 * kXSlot;
-static_assert(kDqLoads * 16 * kDqThreads == kStage, "whole loads per wave");
+constexpr int kXSlot = 64 * 16 * 4;  // a wave's 16 floats per lane
+
+template <int D, int DV>
+struct DqCfg {
+    static constexpr int kKRow = 2 * D, kVRow = 2 * DV;  // bytes per row
+    static constexpr int kKTile = 32 * kKRow, kVTile = 32 * kVRow;
+    static constexpr int kStage = 2 * kKTile + kVTile;   // K1 | K2 | V
+    static constexpr int kLoads = kStage / (16 * kDqThreads);
+    static constexpr int kKChunks = kKTile / 16;
+    static constexpr int kNKB = D / 16;                  // score products per tile
+    static constexpr int kNVH = DV / 32;                 // dP products over half of dv
+    static constexpr int kNCB = D / 32;                  // 32-row blocks of dQ^T
+    static constexpr int kSmem = kDqStages * kStage + 8 * kXSlot;
+    static_assert(kLoads * 16 * kDqThreads == kStage, "whole loads per wave");
+    static_assert(kKChunks % 64 == 0, "a load instruction stays in one tile");
+    static_assert((kStage & (kStage - 1)) == 0 && kStage >= 2 * kVTile,
+                  "stage bases must leave the in-tile address bits free");
+};
 
 // One tile (K1 | K2 | V, 32 rows each) into a ring stage with 8 waves: load
-// instruction i of wave w fills chunk positions 512 i + 64 w .. + 63 (i = 0:
-// K1, 1: K2, 2 and 3: V), each lane fetching the chunk the swizzle puts at
-// its position.
+// instruction i of wave w fills chunk positions 512 i + 64 w .. + 63, which
+// lie in one of the three tiles (a wave-uniform choice of descriptor), each
+// lane fetching the chunk the swizzle puts at its position.
+template <int D, int DV>
 struct TileFeed8 {
-    int off[kDqLoads];
+    using C = DqCfg<D, DV>;
+    int off[C::kLoads];
     __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-        for (int i = 0; i < kDqLoads; ++i) {
+        for (int i = 0; i < C::kLoads; ++i) {
             const int p = 512 * i + 64 * wave + lane;
-            if (p < 1024) {
-                const int q = p & 511, row = q >> 4;
-                off[i] = row * kKRow + 16 * ((q & 15) ^ rswz(row));
+            if (p < 2 * C::kKChunks) {
+                constexpr int cpr = C::kKRow / 16;
+                const int q = p % C::kKChunks, row = q / cpr;
+                off[i] = row * C::kKRow + 16 * ((q % cpr) ^ swz<C::kKRow>(row));
             } else {
-                const int q = p - 1024, row = q >> 5;
-                off[i] = row * kVRow + 16 * ((q & 31) ^ rswz(row));
+                constexpr int cpr = C::kVRow / 16;
+                const int q = p - 2 * C::kKChunks, row = q / cpr;
+                off[i] = row * C::kVRow + 16 * ((q % cpr) ^ swz<C::kVRow>(row));
             }
         }
     }
@@ -271,14 +303,14 @@ struct TileFeed8 {
                                           const uint8_t* k2, const uint8_t* v, int64_t row0,
                                           int64_t n) const {
         const int64_t left = n - row0;
-        const i32x4 r1 = sgpr_rsrc(k1 + row0 * kKRow, left * kKRow);
-        const i32x4 r2 = sgpr_rsrc(k2 + row0 * kKRow, left * kKRow);
-        const i32x4 rv = sgpr_rsrc(v + row0 * kVRow, left * kVRow);
+        const i32x4 r1 = sgpr_rsrc(k1 + row0 * C::kKRow, left * C::kKRow);
+        const i32x4 r2 = sgpr_rsrc(k2 + row0 * C::kKRow, left * C::kKRow);
+        const i32x4 rv = sgpr_rsrc(v + row0 * C::kVRow, left * C::kVRow);
 #pragma unroll
-        for (int i = 0; i < kDqLoads; ++i) {
-            const uint32_t m0 =
-                __builtin_amdgcn_readfirstlane(stage + (uint32_t)(16 * (512 * i + 64 * wave)));
-            load_lds(m0, off[i], i == 0 ? r1 : (i == 1 ? r2 : rv));
+        for (int i = 0; i < C::kLoads; ++i) {
+            const int p0 = 512 * i + 64 * wave;  // wave-uniform
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + (uint32_t)(16 * p0));
+            load_lds(m0, off[i], p0 < C::kKChunks ? r1 : (p0 < 2 * C::kKChunks ? r2 : rv));
         }
     }
 };
@@ -286,13 +318,15 @@ struct TileFeed8 {
 // Workgroup = 128 query rows of one (batch, head); wave w owns rows
 // 32 (w mod 4) .. and map w / 4.  Two sweeps over the key tiles (delta first,
 // then dQ; see the file comment).  Per tile each wave forms its map's scores
-// S^T = K Q^T (8 products) and dP^T over its map's half of the dv channels
-// (8 products), and the two waves of a query block add their halves through
-// LDS: both compute own + partner, and fp32 addition commutes, so they hold
-// the same dP.  Sweep 2 adds dQ^T += K^T dS^T (8 products).
-template <bool CAUSAL>
+// S^T = K Q^T (d/16 products) and dP^T over its map's half of the dv
+// channels (dv/32), and the two waves of a query block add their halves
+// through LDS: both compute own + partner, and fp32 addition commutes, so
+// they hold the same dP.  Sweep 2 adds dQ^T += K^T dS^T (d/16 products).
+template <int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kDqSmem];
+    using C = DqCfg<D, DV>;
+    constexpr int kKRow = C::kKRow, kVRow = C::kVRow, kKTile = C::kKTile, kStage = C::kStage;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int l32 = lane & 31, lh = lane >> 5;
@@ -314,16 +348,16 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
     const uint8_t* gdd = (const uint8_t*)a.dd + (size_t)bh * a.Nq * kVRow;
 
     // B operands of this lane's query (column l32): Q^T of the wave's map over
-    // d, dD^T over the map's half of dv (channels 128 map ..)
-    bf16x8 qf[kNKB], df[kNVB / 2];
+    // d, dD^T over the map's half of dv (channels dv/2 map ..)
+    bf16x8 qf[C::kNKB], df[C::kNVH];
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb)
+    for (int kb = 0; kb < C::kNKB; ++kb)
         qf[kb] = qok ? *(const bf16x8*)(gq + (size_t)qrow * kKRow + 2 * (16 * kb + 8 * lh))
                      : bf16x8{};
 #pragma unroll
-    for (int c = 0; c < kNVB / 2; ++c)
+    for (int c = 0; c < C::kNVH; ++c)
         df[c] = qok ? *(const bf16x8*)(gdd + (size_t)qrow * kVRow +
-                                       2 * (kDV / 2 * map + 16 * c + 8 * lh))
+                                       2 * (DV / 2 * map + 16 * c + 8 * lh))
                     : bf16x8{};
     // keys visible to this lane's query: 0 .. key_end - 1
     const int key_end = qok ? (CAUSAL ? min(a.Nk, qrow + 1) : a.Nk) : 0;
@@ -333,14 +367,14 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
     // first use inside the loop would wait for the ring's loads as well (on
     // every tile).  Used here, before the ring starts, they are complete.
 #pragma unroll
-    for (int kb = 0; kb < kNKB; ++kb) asm volatile("" ::"v"(qf[kb]));
+    for (int kb = 0; kb < C::kNKB; ++kb) asm volatile("" ::"v"(qf[kb]));
 #pragma unroll
-    for (int c = 0; c < kNVB / 2; ++c) asm volatile("" ::"v"(df[c]));
+    for (int c = 0; c < C::kNVH; ++c) asm volatile("" ::"v"(df[c]));
     asm volatile("" ::"v"(lse));
 
-    f32x16 dq[kNCB];
+    f32x16 dq[C::kNCB];
 #pragma unroll
-    for (int cb = 0; cb < kNCB; ++cb) dq[cb] = f32x16{};
+    for (int cb = 0; cb < C::kNCB; ++cb) dq[cb] = f32x16{};
     float dsum = 0.f;
 
     const int nkt_all = (a.Nk + 31) / 32;
@@ -348,7 +382,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
     // key tiles in which some key is visible to some row of this query block
     const int nkt_w = CAUSAL ? min(nkt, (qw0 + 31) / 32 + 1) : nkt;
     const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-    TileFeed8 feed;
+    TileFeed8<D, DV> feed;
     feed.init(wave, lane);
     // The key tiles are swept twice, as one sequence of 2 nkt ring entries:
     // entry g is key tile g mod nkt, in ring stage g mod 3.  Entries past the
@@ -364,7 +398,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
     // waits for entry g, refills the stage entry g - 1 used, returns entry g's
     // stage base
     auto next = [&]() {
-        wait_loads<kDqLoads>();
+        wait_loads<C::kLoads>();
         __syncthreads();
         issue(g + 2, st == 0 ? 2 : st - 1);
         const int sb = st * kStage;
@@ -373,11 +407,11 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
         return sb;
     };
     const int kr = swap23(l32);
-    // the wave's map selects the K tile (bit 13: K2 is 8 KB on) and the half
-    // of each V row (bit 8: its second 256 bytes)
-    const int yk = row_base<kKRow>(kr, lh) | (map << 13);
-    const int yv = row_base<kVRow>(kr, lh) | (map << 8);
-    const int yc = col_base<kKRow>(lane) | (map << 13);
+    // the wave's map selects the K tile (K2 is kKTile on) and the half of
+    // each V row (the swizzle may move a chunk across the halves: an XOR)
+    const int yk = row_base<kKRow>(kr, lh) | (map * kKTile);
+    const int yv = row_base<kVRow>(kr, lh) ^ (map * (kVRow / 2));
+    const int yc = col_base<kKRow>(lane) | (map * kKTile);
     const int x_own = kDqStages * kStage + kXSlot * wave;
     const int x_oth = kDqStages * kStage + kXSlot * (wave ^ 4);
 
@@ -386,9 +420,9 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
         const int ykt = opaque(yk | sb), yvt = opaque(yv | sb);
         s = dph = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb) s = mfma(lds_row<0>(smem, ykt ^ (32 * kb)), qf[kb], s);
+        for (int kb = 0; kb < C::kNKB; ++kb) s = mfma(lds_row<0>(smem, ykt ^ (32 * kb)), qf[kb], s);
 #pragma unroll
-        for (int c = 0; c < kNVB / 2; ++c)
+        for (int c = 0; c < C::kNVH; ++c)
             dph = mfma(lds_row<2 * kKTile>(smem, yvt ^ (32 * c)), df[c], dph);
     };
     // dP = own half + partner's half (the barrier between writing and reading
@@ -469,7 +503,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
         pack(gr, pg);
         const int yct = opaque(yc | sb);
 #pragma unroll
-        for (int cb = 0; cb < kNCB; ++cb) {
+        for (int cb = 0; cb < C::kNCB; ++cb) {
             const int a0 = yct ^ (64 * cb);
             dq[cb] = mfma(lds_col<kKRow, 0>(smem, a0), pg[0], dq[cb]);
             dq[cb] = mfma(lds_col<kKRow, 16 * kKRow>(smem, a0), pg[1], dq[cb]);
@@ -482,11 +516,11 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
     wait_loads<0>();  // the zero-filling loads past the end land before exit
 
     if (!qok) return;
-    const float tau = 1.f / sqrtf((float)kD);
+    const float tau = 1.f / sqrtf((float)D);
     const float sc = map ? -a.lam[h] * tau : tau;
-    __bf16* o = (__bf16*)(map ? a.dq2 : a.dq1) + ((size_t)bh * a.Nq + qrow) * kD;
+    __bf16* o = (__bf16*)(map ? a.dq2 : a.dq1) + ((size_t)bh * a.Nq + qrow) * D;
 #pragma unroll
-    for (int cb = 0; cb < kNCB; ++cb) {
+    for (int cb = 0; cb < C::kNCB; ++cb) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             bf16x4 v;
@@ -699,16 +733,33 @@ void bwd_dkdv_ring_kernel(BackwardArgs a) {
 
 }  // namespace
 
+namespace {
+// the dQ kernel with paired map waves (it is written for any (d, dv) whose
+// tiles fit its ring; at head_dim 64 the one-sweep kernel of backward.hip
+// is faster, so only (128, 256) is instantiated)
+hipError_t launch_bwd_dq_pair(const BackwardArgs& a, int d, int dv, bool causal,
+                              hipStream_t stream) {
+    BackwardArgs copy = a;
+    void* args[] = {&copy};
+    const int64_t g_dq = (int64_t)((a.Nq + kRowsWG - 1) / kRowsWG) * a.B * a.H;
+    if (g_dq > 0x7fffffff) return hipErrorInvalidValue;
+    const void* fn;
+    if (d == 128 && dv == 256)
+        fn = causal ? (const void*)bwd_dq_pair_kernel<128, 256, true>
+                    : (const void*)bwd_dq_pair_kernel<128, 256, false>;
+    else
+        return hipErrorInvalidValue;
+    return hipLaunchKernel(fn, dim3((unsigned)g_dq), dim3(kDqThreads), args, 0, stream);
+}
+}  // namespace
+
 hipError_t launch_backward_ring(const BackwardArgs& a, bool causal, hipStream_t stream) {
     BackwardArgs copy = a;
     void* args[] = {&copy};
     const int64_t BH = (int64_t)a.B * a.H;
-    const int64_t g_dq = (int64_t)((a.Nq + kRowsWG - 1) / kRowsWG) * BH;
     const int64_t g_kv = (int64_t)((a.Nk + kRowsWG - 1) / kRowsWG) * BH;
-    if (g_dq > 0x7fffffff || g_kv > 0x7fffffff) return hipErrorInvalidValue;
-    hipError_t e = hipLaunchKernel(causal ? (const void*)bwd_dq_pair_kernel<true>
-                                          : (const void*)bwd_dq_pair_kernel<false>,
-                                   dim3((unsigned)g_dq), dim3(kDqThreads), args, 0, stream);
+    if (g_kv > 0x7fffffff) return hipErrorInvalidValue;
+    hipError_t e = launch_bwd_dq_pair(a, kD, kDV, causal, stream);
     if (e != hipSuccess) return e;
     return hipLaunchKernel(causal ? (const void*)bwd_dkdv_ring_kernel<true>
                                   : (const void*)bwd_dkdv_ring_kernel<false>,

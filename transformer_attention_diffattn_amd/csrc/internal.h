@@ -124,6 +124,7 @@ hipError_t launch_prefill_twopass(const PrefillArgs& a, int d, int dv, bool caus
 // dQ and dK/dV kernels of the head_dim-128, v_dim-256 backward (after the dD
 // prep, before the dlambda sum)
 hipError_t launch_backward_ring(const BackwardArgs& a, bool causal, hipStream_t stream);
+
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, int dv, bool causal,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int dv, bool bf16, hipStream_t stream);
