@@ -55,52 +55,67 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: dD for every row (one wave per row)
+// prep: dD for every row.  A wave takes kPrepRows rows, lane l elements
+// kPer l .. kPer l + kPer - 1 of each (vector loads), and issues all the
+// rows' loads before the first reduction: with one row per wave the kernel
+// waited out one load latency per row.
 // ---------------------------------------------------------------------------
+constexpr int kPrepRows = 4;
+
 template <int DV>
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BackwardArgs a) {
     constexpr int kPer = DV / 64;
+    typedef float fv __attribute__((ext_vector_type(kPer)));
+    typedef __bf16 bv __attribute__((ext_vector_type(kPer)));
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+    const int64_t row0 = ((int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6)) * kPrepRows;
     const int64_t rows = (int64_t)a.B * a.H * a.Nq;
-    if (row >= rows) return;
-    const float* drow = a.d_save + row * DV;
-    const __bf16* gy = (const __bf16*)a.dout + row * DV;
-    __bf16* out = (__bf16*)a.dd + row * DV;
-    float y[kPer], dd[kPer];
+    if (row0 >= rows) return;
+    fv y[kPrepRows], x[kPrepRows];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) y[i] = (float)gy[lane + 64 * i];
-    if (a.flags & 1u) {
+    for (int j = 0; j < kPrepRows; ++j) {
+        const int64_t row = min(row0 + j, rows - 1);  // (a repeated last row is not stored)
+        const bv yb = *(const bv*)((const __bf16*)a.dout + row * DV + kPer * lane);
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) dd[i] = y[i];
-    } else {
-        float x[kPer], s = 0.f;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            x[i] = drow[lane + 64 * i];
-            s += x[i];
-        }
-        const float mu = wave_sum(s) * (1.f / DV);
-        float q = 0.f;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) q = fmaf(x[i] - mu, x[i] - mu, q);
-        const float inv = 1.f / sqrtf(wave_sum(q) * (1.f / DV) + a.eps);
-        const float c = 1.f - a.lambda_init;
-        float sg = 0.f, sgx = 0.f;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            x[i] = (x[i] - mu) * inv;  // xhat
-            y[i] *= c;                 // g
-            sg += y[i];
-            sgx = fmaf(y[i], x[i], sgx);
-        }
-        const float mg = wave_sum(sg) * (1.f / DV);
-        const float mgx = wave_sum(sgx) * (1.f / DV);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) dd[i] = (y[i] - mg - x[i] * mgx) * inv;
+        for (int i = 0; i < kPer; ++i) y[j][i] = (float)yb[i];
+        if (!(a.flags & 1u)) x[j] = *(const fv*)(a.d_save + row * DV + kPer * lane);
     }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) out[lane + 64 * i] = (__bf16)dd[i];
+    for (int j = 0; j < kPrepRows; ++j) {
+        fv dd;
+        if (a.flags & 1u) {
+            dd = y[j];
+        } else {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) s += x[j][i];
+            const float mu = wave_sum(s) * (1.f / DV);
+            float q = 0.f;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) q = fmaf(x[j][i] - mu, x[j][i] - mu, q);
+            const float inv = 1.f / sqrtf(wave_sum(q) * (1.f / DV) + a.eps);
+            const float c = 1.f - a.lambda_init;
+            float sg = 0.f, sgx = 0.f;
+            fv xh, g;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                xh[i] = (x[j][i] - mu) * inv;
+                g[i] = y[j][i] * c;
+                sg += g[i];
+                sgx = fmaf(g[i], xh[i], sgx);
+            }
+            const float mg = wave_sum(sg) * (1.f / DV);
+            const float mgx = wave_sum(sgx) * (1.f / DV);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) dd[i] = (g[i] - mg - xh[i] * mgx) * inv;
+        }
+        if (row0 + j < rows) {
+            bv ob;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) ob[i] = (__bf16)dd[i];
+            *(bv*)((__bf16*)a.dd + (row0 + j) * DV + kPer * lane) = ob;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -473,11 +488,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dlam_kernel(BackwardArgs a) {
     __shared__ float part[kBwdThreads / 64];
     const int h = blockIdx.x;
     const int64_t BH = (int64_t)a.B * a.H;
-    float s = 0.f;
+    // eight independent partial sums per thread (their loads in flight
+    // together), added in a fixed order: the result does not depend on timing
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int b = 0; b < a.B; ++b) {
         const float* d2 = a.delta + (BH + (int64_t)b * a.H + h) * a.Nq;
-        for (int i = threadIdx.x; i < a.Nq; i += kBwdThreads) s += d2[i];
+        int i = threadIdx.x;
+        for (; i + 7 * kBwdThreads < a.Nq; i += 8 * kBwdThreads) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] += d2[i + u * kBwdThreads];
+        }
+        for (; i < a.Nq; i += kBwdThreads) acc[0] += d2[i];
     }
+    float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
     __syncthreads();
@@ -494,7 +517,7 @@ hipError_t launch_dims(const BackwardArgs& a, bool causal, hipStream_t stream) {
     void* args[] = {&copy};
     const int64_t rows = (int64_t)a.B * a.H * a.Nq;
     const int64_t BH = (int64_t)a.B * a.H;
-    const int64_t g_prep = (rows + 3) / 4;
+    const int64_t g_prep = (rows + 4 * kPrepRows - 1) / (4 * kPrepRows);
     const int64_t g_dq = (int64_t)((a.Nq + 63) / 64) * BH;
     const int64_t g_kv = (int64_t)((a.Nk + 127) / 128) * BH;
     if (g_prep > 0x7fffffff || g_dq > 0x7fffffff || g_kv > 0x7fffffff) return hipErrorInvalidValue;
@@ -528,7 +551,7 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, int d, int dv, bool causa
     if (d == 128 && dv == 256) {
         BackwardArgs copy = a;
         void* args[] = {&copy};
-        const int64_t g_prep = ((int64_t)a.B * a.H * a.Nq + 3) / 4;
+        const int64_t g_prep = ((int64_t)a.B * a.H * a.Nq + 4 * kPrepRows - 1) / (4 * kPrepRows);
         if (g_prep > 0x7fffffff) return hipErrorInvalidValue;
         hipError_t e = hipLaunchKernel((const void*)bwd_prep_kernel<256>, dim3((unsigned)g_prep),
                                        dim3(kBwdThreads), args, 0, stream);
