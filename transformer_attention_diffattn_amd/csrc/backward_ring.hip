@@ -250,6 +250,26 @@ struct TileFeed {
             }
         }
     }
+    // The same with one descriptor per tensor for the whole (batch, head)
+    // slice (under 2 GiB): tile t's rows start t kKTile / t kVTile bytes in,
+    // added to the per-lane offset; t < 0 loads zeros (offsets past the end).
+    __device__ __forceinline__ void issue_flat(uint32_t stage, int wave, const i32x4& r1,
+                                               const i32x4& r2, const i32x4& ry, int t,
+                                               int xend, int yend) const {
+        const int xo = t >= 0 ? t * (32 * kKRow) : xend;
+        const int yo = t >= 0 ? t * (32 * kVRow) : yend;
+#pragma unroll
+        for (int i = 0; i < kTileLoads; ++i) {
+            const uint32_t m0 =
+                __builtin_amdgcn_readfirstlane(stage + (uint32_t)(16 * (256 * i + 64 * wave)));
+            if (i < 4) {
+                load_lds(m0, offx + (i & 1) * 16 * kKRow + xo, i < 2 ? r1 : r2);
+            } else {
+                const int b = 16 * ((2 * (i - 4) + (wave >> 1)) & 3);
+                load_lds(m0, (offy ^ b) + (i - 4) * 8 * kVRow + yo, ry);
+            }
+        }
+    }
 };
 
 // ---------------------------------------------------------------------------
@@ -313,6 +333,22 @@ struct TileFeed8 {
             load_lds(m0, off[i], p0 < C::kKChunks ? r1 : (p0 < 2 * C::kKChunks ? r2 : rv));
         }
     }
+    // one descriptor per tensor for the whole slice (see TileFeed::issue_flat)
+    __device__ __forceinline__ void issue_flat(uint32_t stage, int wave, const i32x4& r1,
+                                               const i32x4& r2, const i32x4& rv, int t,
+                                               int kend, int vend) const {
+        const int ko = t >= 0 ? t * C::kKTile : kend;
+        const int vo = t >= 0 ? t * C::kVTile : vend;
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i) {
+            const int p0 = 512 * i + 64 * wave;  // wave-uniform
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(stage + (uint32_t)(16 * p0));
+            if (p0 < 2 * C::kKChunks)
+                load_lds(m0, off[i] + ko, p0 < C::kKChunks ? r1 : r2);
+            else
+                load_lds(m0, off[i] + vo, rv);
+        }
+    }
 };
 
 // Workgroup = 128 query rows of one (batch, head); wave w owns rows
@@ -322,7 +358,7 @@ struct TileFeed8 {
 // channels (dv/32), and the two waves of a query block add their halves
 // through LDS: both compute own + partner, and fp32 addition commutes, so
 // they hold the same dP.  Sweep 2 adds dQ^T += K^T dS^T (d/16 products).
-template <int D, int DV, bool CAUSAL>
+template <int D, int DV, bool CAUSAL, bool FLAT>
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a) {
     using C = DqCfg<D, DV>;
     constexpr int kKRow = C::kKRow, kVRow = C::kVRow, kKTile = C::kKTile, kStage = C::kStage;
@@ -387,10 +423,18 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
     // The key tiles are swept twice, as one sequence of 2 nkt ring entries:
     // entry g is key tile g mod nkt, in ring stage g mod 3.  Entries past the
     // sequence load zeros (a fixed count per iteration for the waits).
+    // (FLAT: one descriptor per tensor for the (batch, head) slice)
+    const int kbytes = FLAT ? a.Nk * kKRow : 0, vbytes = FLAT ? a.Nk * kVRow : 0;
+    const i32x4 rk1 = sgpr_rsrc(gk1, kbytes), rk2 = sgpr_rsrc(gk2, kbytes);
+    const i32x4 rv = sgpr_rsrc(gv, vbytes);
     auto issue = [&](int g, int st) {
         const int kt = g < nkt ? g : g - nkt;
-        feed.issue(smem_base + (uint32_t)(st * kStage), wave, gk1, gk2, gv, (int64_t)kt * 32,
-                   g < 2 * nkt ? (int64_t)a.Nk : 0);
+        if constexpr (FLAT)
+            feed.issue_flat(smem_base + (uint32_t)(st * kStage), wave, rk1, rk2, rv,
+                            g < 2 * nkt ? kt : -1, kbytes, vbytes);
+        else
+            feed.issue(smem_base + (uint32_t)(st * kStage), wave, gk1, gk2, gv, (int64_t)kt * 32,
+                       g < 2 * nkt ? (int64_t)a.Nk : 0);
     };
     issue(0, 0);
     issue(1, 1);
@@ -539,7 +583,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
 // ---------------------------------------------------------------------------
 // dK_1, dK_2, dV
 // ---------------------------------------------------------------------------
-template <bool CAUSAL>
+template <bool CAUSAL, bool FLAT>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_ring_kernel(BackwardArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (kStage + kRowStage)];
@@ -603,13 +647,25 @@ void bwd_dkdv_ring_kernel(BackwardArgs a) {
     // row terms of the tile's 32 queries: each wave loads its own copy (lanes
     // 32..63 repeat lanes 0..31), so every wave issues the same number of loads
     const int row_off = 16 * l32;
+    // (FLAT: one descriptor per tensor for the (batch, head) slice)
+    const int qbytes = FLAT ? a.Nq * kKRow : 0, dbytes = FLAT ? a.Nq * kVRow : 0;
+    const i32x4 rq1 = sgpr_rsrc(gq1, qbytes), rq2 = sgpr_rsrc(gq2, qbytes);
+    const i32x4 rd = sgpr_rsrc(gdd, dbytes), rr = sgpr_rsrc(grows, FLAT ? a.Nq * 16 : 0);
     auto issue = [&](int qt) {
         const uint32_t sti = (uint32_t)(qt & (kStages - 1));
-        const int64_t n = qt < nqt ? (int64_t)a.Nq : 0;
-        feed.issue(smem_base + sti * kStage, wave_u, gq1, gq2, gdd, (int64_t)qt * 32, n);
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(
             smem_base + kStages * kStage + sti * kRowStage + (uint32_t)(kRowSlot * wave_u));
-        load_lds(m0, row_off, sgpr_rsrc(grows + (int64_t)qt * 32 * 16, (n - (int64_t)qt * 32) * 16));
+        if constexpr (FLAT) {
+            const bool real = qt < nqt;
+            feed.issue_flat(smem_base + sti * kStage, wave_u, rq1, rq2, rd, real ? qt : -1, qbytes,
+                            dbytes);
+            load_lds(m0, row_off + (real ? qt * 32 * 16 : a.Nq * 16), rr);
+        } else {
+            const int64_t n = qt < nqt ? (int64_t)a.Nq : 0;
+            feed.issue(smem_base + sti * kStage, wave_u, gq1, gq2, gdd, (int64_t)qt * 32, n);
+            load_lds(m0, row_off,
+                     sgpr_rsrc(grows + (int64_t)qt * 32 * 16, (n - (int64_t)qt * 32) * 16));
+        }
     };
     issue(qt0);
     issue(qt0 + 1);
@@ -743,12 +799,13 @@ hipError_t launch_bwd_dq_pair(const BackwardArgs& a, int d, int dv, bool causal,
     void* args[] = {&copy};
     const int64_t g_dq = (int64_t)((a.Nq + kRowsWG - 1) / kRowsWG) * a.B * a.H;
     if (g_dq > 0x7fffffff) return hipErrorInvalidValue;
-    const void* fn;
-    if (d == 128 && dv == 256)
-        fn = causal ? (const void*)bwd_dq_pair_kernel<128, 256, true>
-                    : (const void*)bwd_dq_pair_kernel<128, 256, false>;
-    else
-        return hipErrorInvalidValue;
+    if (d != 128 || dv != 256) return hipErrorInvalidValue;
+    // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
+    const bool flat = (int64_t)a.Nk * 2 * dv + 64 * 1024 < (int64_t)0x7fffffff;
+    const void* fn = causal ? (flat ? (const void*)bwd_dq_pair_kernel<128, 256, true, true>
+                                    : (const void*)bwd_dq_pair_kernel<128, 256, true, false>)
+                            : (flat ? (const void*)bwd_dq_pair_kernel<128, 256, false, true>
+                                    : (const void*)bwd_dq_pair_kernel<128, 256, false, false>);
     return hipLaunchKernel(fn, dim3((unsigned)g_dq), dim3(kDqThreads), args, 0, stream);
 }
 }  // namespace
@@ -761,9 +818,12 @@ hipError_t launch_backward_ring(const BackwardArgs& a, bool causal, hipStream_t 
     if (g_kv > 0x7fffffff) return hipErrorInvalidValue;
     hipError_t e = launch_bwd_dq_pair(a, kD, kDV, causal, stream);
     if (e != hipSuccess) return e;
-    return hipLaunchKernel(causal ? (const void*)bwd_dkdv_ring_kernel<true>
-                                  : (const void*)bwd_dkdv_ring_kernel<false>,
-                           dim3((unsigned)g_kv), dim3(kBwdThreads), args, 0, stream);
+    const bool flat = (int64_t)a.Nq * kVRow + 64 * 1024 < (int64_t)0x7fffffff;
+    const void* fn = causal ? (flat ? (const void*)bwd_dkdv_ring_kernel<true, true>
+                                    : (const void*)bwd_dkdv_ring_kernel<true, false>)
+                            : (flat ? (const void*)bwd_dkdv_ring_kernel<false, true>
+                                    : (const void*)bwd_dkdv_ring_kernel<false, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)g_kv), dim3(kBwdThreads), args, 0, stream);
 }
 
 }  // namespace diffattn
