@@ -4,6 +4,7 @@
     python3 profile_kernels.py run [--out DIR]
     python3 profile_kernels.py summarize [--out DIR]
     python3 profile_kernels.py counters [--workload NAME] [--out DIR]
+    python3 profile_kernels.py counters --backward [--out DIR]
 
 (DIR: where rocprofv3 writes its raw output, default prof_out/.)
 
@@ -311,11 +312,22 @@ SIMDS = 256 * 4
 XCDS = 8
 
 
-def _counter_cmd(out: str, i: int, workload: str):
+# the backward kernels, each on the one workload it runs on in bench.py's
+# backward legs (the head_dim-64 pair on the 2K workload, the head_dim-128
+# pair on the large-head one)
+BACKWARD_KERNELS = [
+    ("bwd_dq_kernel", "causal_prefill_bf16"),
+    ("bwd_dkdv_kernel", "causal_prefill_bf16"),
+    ("bwd_dq_pair_kernel", "large_head_bf16"),
+    ("bwd_dkdv_ring_kernel", "large_head_bf16"),
+]
+
+
+def _counter_cmd(out: str, i: int, workload: str, legs: str = "none"):
     py = sys.executable or "python3"
     return ["rocprofv3", "--pmc", *COUNTER_PASSES[i], "-d", os.path.join(out, f"counters{i}"),
             "-o", "run", "-f", "csv", "--", py, os.path.join(ROOT, "bench.py"), "--steps", "3",
-            "--warmup", "1", "--legs", "none", "--workload", workload]
+            "--warmup", "1", "--legs", legs, "--workload", workload]
 
 
 def prefill_kernel_of(workload: str) -> str:
@@ -326,25 +338,37 @@ def prefill_kernel_of(workload: str) -> str:
     return da.prefill_kernel_name(w.d, w.dv, w.dtype)
 
 
-def counters(out: str, workload: str = "long_needles_bf16") -> None:
-    """Runs the counter passes of COUNTER_PASSES over bench.py on one workload."""
+def counters(out: str, workload: str = "long_needles_bf16", backward: bool = False) -> None:
+    """Runs the counter passes of COUNTER_PASSES over bench.py: on one
+    workload's prefill, or (backward) over the two backward legs, whose
+    kernels run only there (the headline prefill runs too, on the 2K
+    workload, and is not summarised)."""
     out = os.path.abspath(out)
     os.makedirs(out, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp")
+    if backward:
+        workload = "causal_prefill_bf16"
     for i in range(len(COUNTER_PASSES)):
-        cmd = _counter_cmd(out, i, workload)
+        cmd = _counter_cmd(out, i, workload, "backward" if backward else "none")
         print(f"[profile] counters pass {i}: {' '.join(cmd)}", flush=True)
         with open(os.path.join(out, f"counters{i}.log"), "w") as log:
             subprocess.run(cmd, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT,
                            timeout=240, check=True)
-    counters_summarize(out, workload, prefill_kernel_of(workload))
+    if backward:
+        for kern, wname in BACKWARD_KERNELS:
+            counters_summarize(out, wname, kern, bench_workload=workload, legs="backward")
+    else:
+        counters_summarize(out, workload, prefill_kernel_of(workload))
 
 
 def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
-                       kernel: str = "prefill_bf16_kernel") -> None:
+                       kernel: str = "prefill_bf16_kernel", bench_workload: str = None,
+                       legs: str = "none") -> None:
     """Per-dispatch SQ counters of one kernel, written to
-    <profiles>/<kernel>__<workload>__counters.md."""
+    <profiles>/<kernel>__<workload>__counters.md.  bench_workload and legs:
+    the bench.py command the passes ran (default: workload, no legs)."""
     out = os.path.abspath(out)
+    bench_workload = bench_workload or workload
     vals = {}
     for i in range(len(COUNTER_PASSES)):
         per = defaultdict(lambda: defaultdict(float))
@@ -378,13 +402,17 @@ def counters_summarize(out: str, workload: str = "causal_prefill_bf16",
             vals.get("SQ_INSTS_VALU_TRANS_F32", 0) / vals["SQ_INSTS_MFMA"])
         derived["LDS instructions per MFMA"] = vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"]
     src = ([e[2] for e in entries() if e[0] == kernel] or [_PREFILL])[0]
+    if not vals:
+        print(f"[profile] {kernel}: no dispatches in the counter passes, skipped", flush=True)
+        return
+    how = "--backward" if legs == "backward" else f"--workload {workload}"
     lines = [f"# {kernel} on {workload}: SQ counters per dispatch", "",
              "Commands (from /tmp, TMPDIR=/tmp; written by "
-             f"`python3 profile_kernels.py counters --workload {workload}`):", ""]
+             f"`python3 profile_kernels.py counters {how}`):", ""]
     py = sys.executable or "python3"
     for i in range(len(COUNTER_PASSES)):
         shown = ["python3" if c == py else (os.path.relpath(c, ROOT) if c.startswith(ROOT) else c)
-                 for c in _counter_cmd(os.path.relpath(out, ROOT), i, workload)]
+                 for c in _counter_cmd(os.path.relpath(out, ROOT), i, bench_workload, legs)]
         lines.append(f"- `{' '.join(shown)}`")
     lines += ["", "Kernel cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); "
               "SIMD cycles = kernel cycles x 1024 SIMDs (256 CUs x 4).", "",
@@ -423,6 +451,8 @@ if __name__ == "__main__":
     ap.add_argument("action", choices=["run", "summarize", "counters", "counters-summarize"])
     ap.add_argument("--out", default=os.path.join(ROOT, "prof_out"))
     ap.add_argument("--workload", default="long_needles_bf16")
+    ap.add_argument("--backward", action="store_true",
+                    help="counters: the backward legs' kernels instead of a prefill")
     ap.add_argument("--profiles-dir", default=PROFILES,
                     help="where summaries go (on a remote GPU box: a folder that is copied back)")
     a = ap.parse_args()
@@ -432,6 +462,10 @@ if __name__ == "__main__":
     elif a.action == "summarize":
         summarize(a.out)
     elif a.action == "counters":
-        counters(a.out, a.workload)
+        counters(a.out, a.workload, a.backward)
+    elif a.backward:
+        for kern, wname in BACKWARD_KERNELS:
+            counters_summarize(a.out, wname, kern, bench_workload="causal_prefill_bf16",
+                               legs="backward")
     else:
         counters_summarize(a.out, a.workload, prefill_kernel_of(a.workload))
