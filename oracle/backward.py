@@ -105,35 +105,57 @@ def head_backward(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
     return dq1, dq2, dk1, dk2, dv, dlam
 
 
-def head_magnitudes(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
-                    lambda_init: float = 0.8, eps: float = 1e-5, pre_norm: bool = False):
-    """Per gradient element of one head, the sum of the absolute values of
-    the terms that make it up, one level down the chain rule: with
-    |dA|_ij = sum_c |dD_ic| |V_jc| and delta_k = rowsum(A_k * dA_k),
-      dQ_k: tau c_k sum_j A_k,ij (|dA|_ij + |delta_k,i|) |K_k,jc|,
-      dK_k: tau c_k sum_i A_k,ij (|dA|_ij + |delta_k,i|) |Q_k,ic|,
-      dV:   sum_i (A_1,ij + |lambda| A_2,ij) |dD_ic|,
-    with c_1 = 1, c_2 = |lambda|.  Every gradient is bounded by it in
-    absolute value (the triangle inequality on the expressions of
-    head_backward), and a computation that rounds a factor of each term to a
-    format with unit roundoff u is off by at most a small multiple of u times
-    it: the bound a bf16 kernel is held to where heavy-tailed inputs make a
-    few terms far larger than their sum.  Returns (mq1, mq2, mk1, mk2, mv)."""
+def head_error_scales(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,
+                      lambda_init: float = 0.8, eps: float = 1e-5, pre_norm: bool = False):
+    """Per gradient element of one head, the error a computation with bf16
+    factors can leave in it, in units of the format's unit roundoff u: the
+    root-sum-square over the element's terms of each term's error scale,
+    plus the part that cannot average out.  The model (fp32 sums, factors
+    rounded to bf16, every rounding off by at most u relative):
+      * dD: each entry off by u (|dD_ic| + s_i), s_i = rms_c dD_ic (its own
+        rounding, and what it inherits through the normalisation's row
+        statistics from the saved forward D);
+      * dA_ij = sum_c dD_ic V_jc: off by u E_ij, E_ij = sqrt(sum_c
+        (|dD_ic| + s_i)^2 V_jc^2) (independent errors over c);
+      * A recomputed from the saved log-sum-exp: off by u relative, the same
+        factor along a row (the row sum it comes from adds up rounded terms);
+      * delta_i = sum_j A_ij dA_ij: off by u e_i, e_i = sqrt(sum_j A_ij^2
+        E_ij^2) + |delta_i|;
+      * dS_ij = A_ij (dA_ij - delta_i), rounded: off by u T_ij,
+        T_ij = 2 |dS_ij| + A_ij (E_ij + e_i);
+      * dQ_k,ic = tau c_k sum_j dS_ij K_jc: tau c_k (sqrt(sum_j T_ij^2
+        K_jc^2) + |delta_i| |sum_j A_ij K_jc|), the last term being the row's
+        common error of A, which does not average out over j;
+        dK_k,jc: tau c_k sqrt(sum_i T_ij^2 Q_ic^2);
+      * dV_jc = sum_i W_ij dD_ic, W = A_1 - lambda A_2 rounded:
+        sqrt(sum_i ((A_1 + |lambda| A_2)_ij (3 |dD_ic| + s_i))^2);
+    with c_1 = 1, c_2 = |lambda|.  The term errors are independent roundings,
+    each of standard deviation at most u/sqrt(3) times its bound, so an
+    element's error has a standard deviation of at most u R / sqrt(3) and a
+    bound of 4 u R sits ~7 standard deviations out; the gradient's own
+    rounding to bf16 adds u |g|.  Returns (rq1, rq2, rk1, rk2, rv)."""
     q1, q2, k1, k2, v, dout = (_f64(t) for t in (q1, q2, k1, k2, v, dout))
     d = q1.shape[1]
     tau = 1.0 / np.sqrt(d)
     a1 = _softmax_rows(_scores(q1, k1, causal))
     a2 = _softmax_rows(_scores(q2, k2, causal))
     dD = _norm_backward(a1 @ v - lam * (a2 @ v), dout, lambda_init, eps, pre_norm)
+    s = np.sqrt((dD * dD).mean(axis=1, keepdims=True))
+    e_dd = np.abs(dD) + s
     da = dD @ v.T
-    absda = np.abs(dD) @ np.abs(v).T
+    E = np.sqrt((e_dd * e_dd) @ (v * v).T)
     out = []
     for a, c, q, k in ((a1, 1.0, q1, k1), (a2, abs(lam), q2, k2)):
         delta = (a * da).sum(axis=1, keepdims=True)
-        t = a * (absda + np.abs(delta))
-        out.append((tau * c * (t @ np.abs(k)), tau * c * (t.T @ np.abs(q))))
-    mv = (a1 + abs(lam) * a2).T @ np.abs(dD)
-    return out[0][0], out[1][0], out[0][1], out[1][1], mv
+        e_delta = np.sqrt(((a * E) ** 2).sum(axis=1, keepdims=True)) + np.abs(delta)
+        T = 2.0 * np.abs(a * (da - delta)) + a * (E + e_delta)
+        rq = tau * c * (np.sqrt((T * T) @ (k * k)) + np.abs(delta) * np.abs(a @ k))
+        rk = tau * c * np.sqrt((T * T).T @ (q * q))
+        out.append((rq, rk))
+    w = a1 + abs(lam) * a2
+    tv = 3.0 * np.abs(dD) + s
+    rv = np.sqrt((w * w).T @ (tv * tv))
+    return out[0][0], out[1][0], out[0][1], out[1][1], rv
 
 
 def head_dlambda_terms(q1, q2, k1, k2, v, lam: float, dout, *, causal: bool,

@@ -4,7 +4,7 @@ Tolerances, from the arithmetic:
 * row max: the largest scaled score, formed from exact bf16 products summed
   in fp32 (d terms): within 1e-4 (1 + |oracle|);
 * needle weights: exp(S - lse) with fp32 scores and the training forward's
-  log-sum-exp, which is off by at most ~2^-9 (its row sum is taken over
+  log-sum-exp, which is off by at most ~2^-8 (its row sum is taken over
   bf16-rounded probabilities): within 1e-2 relative + 1e-6.
 """
 import numpy as np
