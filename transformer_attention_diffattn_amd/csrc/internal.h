@@ -65,7 +65,7 @@ struct BackwardArgs {
     float* dlam;         // [H]
     void* dd;            // workspace: dD [B][H][Nq][dv] bf16
     float* delta;        // workspace: [2][B][H][Nq] row terms sum_j P_k dP
-    float* rows;         // workspace: [B][H][Nq][4] lse_1, lse_2 (log2 units), delta_1, delta_2
+    float* rows;         // workspace: [B][H][Nq][4] lse_1, delta_1, lse_2, delta_2 (lse in log2 units)
     int32_t B, H, Nq, Nk;
     float lambda_init;
     float eps;
