@@ -85,7 +85,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -161,26 +160,31 @@ __device__ __forceinline__ i32x4 sgpr_rsrc(const void* base, int64_t bytes) {
     return r;
 }
 
-// The two fp16 halves of a 32-bit word.  Taking the word by value matters:
-// applied directly to an element of a vector (v[i]), the compiler's
-// __builtin_bit_cast reads element 0 whatever i is.
-__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
-
 // P = x1 - x2 for the 8 weight pairs of a tile as own + partner: the first
 // map's wave stores x1, the lambda map's wave -x2, each keeps its own values
-// and reads the other's (two 16-byte reads); fp16 addition commutes, so both
-// waves get the same bits.  Rounded to bf16 in B-operand order (registers
-// 8kb .. 8kb+7).
+// and reads the other's (two 16-byte reads).  Each sum is formed in fp32 as
+// fma(own, one, other) on the fp16 halves -- the compiler selects
+// v_fma_mix_f32, which converts and adds in one instruction, when the fp16
+// one is not a constant it could fold -- exactly (two fp16 values sum
+// exactly in fp32 unless their exponents differ by more than 12); fp32
+// addition commutes, so both waves get the same bits.  Rounded once to bf16
+// in B-operand order (registers 8kb .. 8kb+7).
 __device__ __forceinline__ void combine(const u32x4 (&own)[2], const u32x4 (&other)[2], bf16x8 (&pb)[2]) {
+    uint32_t one_bits = 0x3c00u;  // fp16 1.0
+    asm volatile("" : "+s"(one_bits));
+    const float one = (float)__builtin_bit_cast(_Float16, (uint16_t)one_bits);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const u32x4 v1 = own[kb], v2 = other[kb];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t w1 = v1[c], w2 = v2[c];
-            const f16x2 d = as_f16x2(w1) + as_f16x2(w2);
-            pb[kb][2 * c] = (__bf16)(float)d[0];
-            pb[kb][2 * c + 1] = (__bf16)(float)d[1];
+            const _Float16 a0 = __builtin_bit_cast(_Float16, (uint16_t)w1);
+            const _Float16 a1 = __builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16));
+            const _Float16 b0 = __builtin_bit_cast(_Float16, (uint16_t)w2);
+            const _Float16 b1 = __builtin_bit_cast(_Float16, (uint16_t)(w2 >> 16));
+            pb[kb][2 * c] = (__bf16)__builtin_fmaf((float)a0, one, (float)b0);
+            pb[kb][2 * c + 1] = (__bf16)__builtin_fmaf((float)a1, one, (float)b1);
         }
     }
 }
