@@ -44,6 +44,10 @@
 
 #include <math.h>
 
+// The direct-to-LDS loads set M0 in inline asm; nothing else in this file
+// uses M0, so the reserved-register clobber is safe here.
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace diffattn {
 namespace {
 
