@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DIFFATTN_ABI_VERSION 1
+#define DIFFATTN_ABI_VERSION 2
 
 /* element types */
 #define DIFFATTN_F32 0
@@ -61,6 +61,13 @@ extern "C" {
 /* flags */
 #define DIFFATTN_FLAG_PRE_NORM 1u  /* write D itself: skip the GroupNorm and the
                                       (1 - lambda_init) scale (for checks) */
+#define DIFFATTN_FLAG_TILE_DESCRIPTORS 2u
+/* Prefill, training forward and backward kernels address each K/V (or Q/dD)
+ * tile through a buffer descriptor of its own when a (batch, head) slice of a
+ * tensor spans 2 GiB or more, and through one descriptor per tensor below
+ * that.  This flag selects the per-tile form at any size; the results are
+ * bitwise the same (for checks of the large-tensor path at small sizes).
+ * Decode, diagnostics and the projection ignore it. */
 
 /*
  * Problem sizes.  Supported (head_dim, v_dim) pairs: (32, 64), (64, 128),

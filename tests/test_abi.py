@@ -32,7 +32,7 @@ def _decode(dims, cap=16, ws=None, ws_bytes=0, splits=1, ptrs=None, lens=None, l
 
 
 def test_library_loads_and_reports_version():
-    assert da.abi_version() == 1
+    assert da.abi_version() == 2
 
 
 def test_exports_every_declared_function():
@@ -74,7 +74,7 @@ def test_fwd_rejects_misaligned_pointers(i):
     ("batch", 0, da.ERR_INVALID), ("heads", -1, da.ERR_INVALID), ("seq_q", 0, da.ERR_INVALID),
     ("seq_k", 0, da.ERR_INVALID), ("head_dim", 0, da.ERR_INVALID), ("v_dim", 0, da.ERR_INVALID),
     ("eps", -1e-3, da.ERR_INVALID), ("eps", float("nan"), da.ERR_INVALID),
-    ("eps", float("inf"), da.ERR_INVALID), ("flags", 2, da.ERR_INVALID),
+    ("eps", float("inf"), da.ERR_INVALID), ("flags", 4, da.ERR_INVALID),
     ("dtype", 7, da.ERR_UNSUPPORTED), ("head_dim", 48, da.ERR_UNSUPPORTED),
     ("v_dim", 64, da.ERR_UNSUPPORTED), ("seq_k", (1 << 30) + 1, da.ERR_UNSUPPORTED),
 ])

@@ -29,6 +29,7 @@ __all__ = [
     "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "decode_workspace_size", "decode_default_splits", "abi_version", "library_path",
     "prefill_kernel_name", "DiffAttnError", "SUPPORTED_DIMS", "FLAG_PRE_NORM",
+    "FLAG_TILE_DESCRIPTORS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +40,7 @@ _HEADER = os.path.join(os.path.dirname(_HERE), "include", "diffattn.h")
 SUPPORTED_DIMS = ((32, 64), (64, 128), (128, 256))
 F32, BF16 = 0, 1
 FLAG_PRE_NORM = 1
+FLAG_TILE_DESCRIPTORS = 2
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 NOALLOC_SCRATCH_BYTES = 16 << 20  # DIFFATTN_NOALLOC_SCRATCH_BYTES
 
@@ -162,6 +164,13 @@ def _lam_tensor(lam, H: int, device) -> torch.Tensor:
     return t.contiguous()
 
 
+def _flags(pre_norm: bool, tile_descriptors: bool) -> int:
+    """DIFFATTN_FLAG_* bits: pre_norm writes D itself; tile_descriptors makes
+    the kernels address every tile through its own buffer descriptor, as they
+    do for (batch, head) slices of 2 GiB or more (same results)."""
+    return (FLAG_PRE_NORM if pre_norm else 0) | (FLAG_TILE_DESCRIPTORS if tile_descriptors else 0)
+
+
 def _require(ok: bool, msg: str):
     if not ok:
         raise ValueError(msg)
@@ -170,11 +179,13 @@ def _require(ok: bool, msg: str):
 def fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
         v: torch.Tensor, lam: Union[float, Sequence[float], torch.Tensor],
         lambda_init: float = 0.8, causal: bool = True, eps: float = 1e-5,
-        out: Optional[torch.Tensor] = None, pre_norm: bool = False) -> torch.Tensor:
+        out: Optional[torch.Tensor] = None, pre_norm: bool = False,
+        tile_descriptors: bool = False) -> torch.Tensor:
     """Fused prefill.  q1, q2 [B,H,Nq,d]; k1, k2 [B,H,Nk,d]; v [B,H,Nk,dv]; all
     bf16 or all fp32, contiguous, on one GPU.  lam: scalar or [H].  Returns
     out [B,H,Nq,dv] in the input dtype.  pre_norm=True returns
-    D = (A1 - lam A2) V without the GroupNorm and scale."""
+    D = (A1 - lam A2) V without the GroupNorm and scale; tile_descriptors, see
+    _flags."""
     ts = (q1, q2, k1, k2, v)
     _require(all(t.is_cuda for t in ts), "inputs must be GPU tensors")
     _require(all(t.device == q1.device for t in ts), "inputs must share one device")
@@ -192,7 +203,7 @@ def fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
              and out.device == q1.device, "out must be a contiguous [B,H,Nq,dv] tensor")
     lam_t = _lam_tensor(lam, H, q1.device)
     dims = Dims(B, H, Nq, Nk, d, dv, _dtype_code(q1), float(eps),
-                FLAG_PRE_NORM if pre_norm else 0)
+                _flags(pre_norm, tile_descriptors))
     st = lib().diffattn_fwd(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
                             v.data_ptr(), lam_t.data_ptr(), float(lambda_init), int(bool(causal)),
                             out.data_ptr(), ctypes.byref(dims), _stream_ptr(q1.device))
@@ -204,7 +215,7 @@ def fwd_fp8(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tens
             v: torch.Tensor, qk_scales: Sequence[float],
             lam: Union[float, Sequence[float], torch.Tensor], lambda_init: float = 0.8,
             causal: bool = True, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
-            pre_norm: bool = False) -> torch.Tensor:
+            pre_norm: bool = False, tile_descriptors: bool = False) -> torch.Tensor:
     """Prefill with e4m3 queries and keys: q1, q2, k1, k2 are
     torch.float8_e4m3fn (or uint8 codes) [B,H,N,d], v bf16 [B,H,Nk,dv] with
     (d, dv) = (64, 128) or (128, 256); qk_scales the four per-tensor
@@ -230,7 +241,7 @@ def fwd_fp8(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tens
     _require(out.shape == (B, H, Nq, dv) and out.dtype == torch.bfloat16 and out.is_contiguous()
              and out.device == q1.device, "out must be a contiguous bf16 [B,H,Nq,dv] tensor")
     lam_t = _lam_tensor(lam, H, q1.device)
-    dims = Dims(B, H, Nq, Nk, d, dv, BF16, float(eps), FLAG_PRE_NORM if pre_norm else 0)
+    dims = Dims(B, H, Nq, Nk, d, dv, BF16, float(eps), _flags(pre_norm, tile_descriptors))
     scales = (ctypes.c_float * 4)(*sc)
     st = lib().diffattn_fwd_fp8(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
                                 v.data_ptr(), scales, lam_t.data_ptr(), float(lambda_init),
@@ -284,7 +295,7 @@ def _check_inputs(q1, q2, k1, k2, v):
 def fwd_train(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
               v: torch.Tensor, lam: Union[float, Sequence[float], torch.Tensor],
               lambda_init: float = 0.8, causal: bool = True, eps: float = 1e-5,
-              pre_norm: bool = False):
+              pre_norm: bool = False, tile_descriptors: bool = False):
     """Training forward (bf16, d = 32, 64 or 128): returns (out, d_save, lse) with
     d_save = D [B,H,Nq,dv] fp32 and lse [2,B,H,Nq] fp32 (natural-log
     log-sum-exp of each map's score rows), the inputs of ``bwd``."""
@@ -295,7 +306,7 @@ def fwd_train(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
     lse = torch.empty((2, B, H, Nq), dtype=torch.float32, device=dev)
     lam_t = _lam_tensor(lam, H, dev)
     dims = Dims(B, H, Nq, Nk, d, dv, _dtype_code(q1), float(eps),
-                FLAG_PRE_NORM if pre_norm else 0)
+                _flags(pre_norm, tile_descriptors))
     st = lib().diffattn_fwd_train(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
                                   v.data_ptr(), lam_t.data_ptr(), float(lambda_init),
                                   int(bool(causal)), out.data_ptr(), d_save.data_ptr(),
@@ -313,7 +324,8 @@ def bwd_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, dv: int) -> int
 def bwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
         v: torch.Tensor, lam: Union[float, Sequence[float], torch.Tensor], dout: torch.Tensor,
         d_save: torch.Tensor, lse: torch.Tensor, lambda_init: float = 0.8, causal: bool = True,
-        eps: float = 1e-5, pre_norm: bool = False, workspace: Optional[torch.Tensor] = None):
+        eps: float = 1e-5, pre_norm: bool = False, workspace: Optional[torch.Tensor] = None,
+        tile_descriptors: bool = False):
     """Backward of ``fwd_train`` (same arguments): gradients of sum(dout * out).
     Returns (dq1, dq2, dk1, dk2, dv) in the input dtype and dlambda [H] fp32
     (summed over batch and rows; sum it for a scalar lambda)."""
@@ -328,7 +340,7 @@ def bwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
     grads = [torch.empty_like(t) for t in (q1, q2, k1, k2, v)]
     dlam = torch.empty((H,), dtype=torch.float32, device=dev)
     dims = Dims(B, H, Nq, Nk, d, dv, _dtype_code(q1), float(eps),
-                FLAG_PRE_NORM if pre_norm else 0)
+                _flags(pre_norm, tile_descriptors))
     need = int(lib().diffattn_bwd_workspace_size(ctypes.byref(dims)))
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)

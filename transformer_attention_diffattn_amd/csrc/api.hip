@@ -41,7 +41,8 @@ int check_dims(const diffattn_dims* dm) {
         dm->v_dim < 1)
         return DIFFATTN_ERR_INVALID;
     if (!(dm->eps >= 0.f) || !isfinite(dm->eps)) return DIFFATTN_ERR_INVALID;
-    if (dm->flags & ~DIFFATTN_FLAG_PRE_NORM) return DIFFATTN_ERR_INVALID;
+    if (dm->flags & ~(DIFFATTN_FLAG_PRE_NORM | DIFFATTN_FLAG_TILE_DESCRIPTORS))
+        return DIFFATTN_ERR_INVALID;
     if (dm->dtype != DIFFATTN_F32 && dm->dtype != DIFFATTN_BF16) return DIFFATTN_ERR_UNSUPPORTED;
     if (!supported_dims(dm->head_dim, dm->v_dim)) return DIFFATTN_ERR_UNSUPPORTED;
     if ((int64_t)dm->batch * dm->heads > 0x7fffffff) return DIFFATTN_ERR_UNSUPPORTED;

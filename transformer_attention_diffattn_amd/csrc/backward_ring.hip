@@ -805,7 +805,7 @@ hipError_t launch_bwd_dq_pair(const BackwardArgs& a, int d, int dv, bool causal,
     if (g_dq > 0x7fffffff) return hipErrorInvalidValue;
     if (d != 128 || dv != 256) return hipErrorInvalidValue;
     // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
-    const bool flat = (int64_t)a.Nk * 2 * dv + 64 * 1024 < (int64_t)0x7fffffff;
+    const bool flat = one_descriptor(a.flags, (int64_t)a.Nk * 2 * dv);
     const void* fn = causal ? (flat ? (const void*)bwd_dq_pair_kernel<128, 256, true, true>
                                     : (const void*)bwd_dq_pair_kernel<128, 256, true, false>)
                             : (flat ? (const void*)bwd_dq_pair_kernel<128, 256, false, true>
@@ -822,7 +822,7 @@ hipError_t launch_backward_ring(const BackwardArgs& a, bool causal, hipStream_t 
     if (g_kv > 0x7fffffff) return hipErrorInvalidValue;
     hipError_t e = launch_bwd_dq_pair(a, kD, kDV, causal, stream);
     if (e != hipSuccess) return e;
-    const bool flat = (int64_t)a.Nq * kVRow + 64 * 1024 < (int64_t)0x7fffffff;
+    const bool flat = one_descriptor(a.flags, (int64_t)a.Nq * kVRow);
     const void* fn = causal ? (flat ? (const void*)bwd_dkdv_ring_kernel<true, true>
                                     : (const void*)bwd_dkdv_ring_kernel<true, false>)
                             : (flat ? (const void*)bwd_dkdv_ring_kernel<false, true>

@@ -7,6 +7,18 @@
 
 namespace diffattn {
 
+// PrefillArgs / BackwardArgs flags bit of DIFFATTN_FLAG_TILE_DESCRIPTORS:
+// per-tile buffer descriptors at any size
+constexpr uint32_t kFlagTileDescriptors = 2u;
+
+// One buffer descriptor per tensor when the largest (batch, head) slice a
+// kernel loads through one spans less than 2 GiB (its tile offsets, and the
+// past-the-end offset of up to 64 KB, then stay in the 31-bit range), unless
+// the caller asked for per-tile descriptors.
+inline bool one_descriptor(uint32_t flags, int64_t slice_bytes) {
+    return !(flags & kFlagTileDescriptors) && slice_bytes + 64 * 1024 < (int64_t)0x7fffffff;
+}
+
 // Arguments of every prefill kernel.  Pointers are device memory, layouts as in
 // diffattn.h.  Element pointers are untyped; each kernel reinterprets them.
 struct PrefillArgs {

@@ -38,7 +38,7 @@ hipError_t launch_dims(const PrefillArgs& a, bool causal, hipStream_t stream) {
     PrefillArgs copy = a;
     void* args[] = {&copy};
     // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
-    const bool flat = (int64_t)a.Nk * DV * 2 + 64 * 1024 < (int64_t)0x7fffffff;
+    const bool flat = one_descriptor(a.flags, (int64_t)a.Nk * DV * 2);
     const void* fn;
     if constexpr (F8)
         fn = causal ? (flat ? (const void*)prefill_fp8qk_kernel<true, true>

@@ -711,7 +711,7 @@ hipError_t launch_prefill_twopass(const PrefillArgs& a, int d, int dv, bool caus
     PrefillArgs copy = a;
     void* args[] = {&copy};
     // one descriptor per tensor when each (batch, head) slice spans < 2 GiB
-    const bool flat = (int64_t)a.Nk * kVRow + 64 * 1024 < (int64_t)0x7fffffff;
+    const bool flat = one_descriptor(a.flags, (int64_t)a.Nk * kVRow);
     const void* fn;
     if (fp8qk) {
         if (a.lse) return hipErrorInvalidValue;  // no training forward from e4m3 scores
