@@ -6,15 +6,14 @@ slice spans less than 2 GiB, and through one descriptor per tile beyond that.
 Only the second form serves slices of 2 GiB or more; test_parity_gpu.py
 allocates such a slice for the head_dim-32/64 non-causal forward only (over
 8.4M keys), and DIFFATTN_FLAG_TILE_DESCRIPTORS selects the form at any size
-for every other kernel and mode.  The two
-forms load the same bytes into the same LDS places and do the same
-arithmetic, so their results must be bitwise equal -- and the one-descriptor
-results are checked against the oracle by the other GPU tests (one case here
-is also checked against the oracle directly).  Shapes: several tiles with a
+for every other kernel and mode.  The two forms load the same bytes into the
+same LDS places and do the same arithmetic, so their results must be bitwise
+equal -- and the one-descriptor results are checked against the oracle by
+the other GPU tests (one case here is also checked against the oracle
+directly).  Shapes: several tiles with a
 ragged end, causal and not, rectangular, and a (batch * heads) count that is
 not a multiple of 8 (the grid-order fallback).
 """
-import numpy as np
 import pytest
 import torch
 
