@@ -34,7 +34,7 @@
 //   Iteration j of a wave issues, in one branch-free block,
 //     MFMA  scores of tile j+1, P.V of tile j-1;
 //     VALU  probabilities of tile j, row sums;
-//     memory  the global-to-LDS loads of tile j+6 (all waves);
+//     memory  the global-to-LDS loads of tile j+5 (all waves);
 //   and ends with the masking of tile j+1 (tiles on the causal diagonal and
 //   the ragged last tile only) and the lazy-maximum test of tile j (below),
 //   whose body almost never runs.  None of the three streams waits for
@@ -576,12 +576,16 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     //   vector work          the 8 probability pairs of tile j, each in three
     //                        steps (scale, exp2, pack and sum) in consecutive
     //                        slots so that a slot's work is independent,
-    //                        starting in a slot -1 that has no product; the
-    //                        loads of tile j+6 early.
+    //                        starting in a slot -1 that has no product;
+    //   memory               the loads of tile j+5 (kAhead) in slot
+    //                        kLoadSlot, late in the iteration: issued after
+    //                        most of its LDS operand reads rather than among
+    //                        them (slot 8 against slot 1, same box: -1.6% and
+    //                        -2.4% on the 32K workload, -1.3% on the 2K one).
     constexpr int kPairsV = 2 * NDB;  // V operands (db, kb)
     constexpr int kSlots = NKS + kPairsV;
     constexpr int kLookahead = 3;
-    constexpr int kLoadSlot = 1;
+    constexpr int kLoadSlot = kSlots > 8 ? 8 : kSlots - 1;
     // probability pair k (registers 2k, 2k+1) starts in slot pair_slot(k)
     auto pair_slot = [](int k) { return k * (kSlots - 3) / 8 - 1; };
     static_assert(7 * (kSlots - 3) / 8 - 1 + 2 < kSlots, "pairs must finish in the slots");
