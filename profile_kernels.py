@@ -454,7 +454,7 @@ if __name__ == "__main__":
     ap.add_argument("--backward", action="store_true",
                     help="counters: the backward legs' kernels instead of a prefill")
     ap.add_argument("--profiles-dir", default=PROFILES,
-                    help="where summaries go (on a remote GPU box: a folder that is copied back)")
+                    help="where the summaries go (default: profiles/)")
     a = ap.parse_args()
     PROFILES = os.path.abspath(a.profiles_dir)
     if a.action == "run":

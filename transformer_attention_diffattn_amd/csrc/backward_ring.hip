@@ -447,8 +447,8 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_pair_kernel(BackwardArgs a)
     // entry g + 2 into the stage entry g - 1 used.  The refill comes after the
     // tile's score and dP products: its loads, which the compiler may not
     // move LDS reads across, then no longer hold back that step's operand
-    // reads (same box: 11.76 -> 11.35 ms for the backward with the same
-    // change in the dK/dV kernel).
+    // reads (measured back to back on one GPU: 11.76 -> 11.35 ms for the
+    // backward with the same change in the dK/dV kernel).
     int pend_g = 0, pend_st = 0;
     auto refill = [&]() { issue(pend_g, pend_st); };
     auto next = [&]() {

@@ -580,8 +580,9 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
     //   memory               the loads of tile j+5 (kAhead) in slot
     //                        kLoadSlot, late in the iteration: issued after
     //                        most of its LDS operand reads rather than among
-    //                        them (slot 8 against slot 1, same box: -1.6% and
-    //                        -2.4% on the 32K workload, -1.3% on the 2K one).
+    //                        them (slot 8 against slot 1, back to back on one
+    //                        GPU: -1.6% and -2.4% on the 32K workload, -1.3%
+    //                        on the 2K one).
     constexpr int kPairsV = 2 * NDB;  // V operands (db, kb)
     constexpr int kSlots = NKS + kPairsV;
     constexpr int kLookahead = 3;
