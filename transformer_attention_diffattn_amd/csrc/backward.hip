@@ -379,7 +379,11 @@ void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
         for (int c = 0; c < NVB; ++c) dp = mfma(ad[c], vf[c], dp);
         // the transposed operands of the dV and dK products (independent of
-        // the vector work below) and the row terms, in flight meanwhile
+        // the vector work below), in flight meanwhile.  The row terms are
+        // read where they are used: held for all 16 rows they took 64
+        // registers, whose copies to and from the accumulation registers
+        // cost more than the reads' latency (2K workload backward 0.536 ->
+        // 0.500 ms, back to back on one GPU).
         bf16x8 ov[2][NDB], o1c[2][NCB], o2c[2][NCB];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -391,9 +395,6 @@ void bwd_dkdv_kernel(BackwardArgs a) {
                 o2c[kk][cb] = rd_col(sq2, KS, 16 * kk, 32 * cb, lane);
             }
         }
-        float4 trow[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) trow[r] = sr[16 * (r >> 3) + 8 * lh + (r & 7)];
         __builtin_amdgcn_sched_barrier(0);
         float wd[16], d1[16], d2[16];
         // the mask is needed only where the tile meets the diagonal or a
@@ -403,7 +404,7 @@ void bwd_dkdv_kernel(BackwardArgs a) {
         auto probs = [&](auto masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float4 t = trow[r];
+                const float4 t = sr[16 * (r >> 3) + 8 * lh + (r & 7)];
                 float x1 = fmaf(s1[r], sl2, -t.x), x2 = fmaf(s2[r], sl2, -t.y);
                 if constexpr (decltype(masked)::value) {
                     const int qi = 16 * (r >> 3) + 8 * lh + (r & 7);
