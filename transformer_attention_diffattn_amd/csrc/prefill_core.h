@@ -480,15 +480,16 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
         for (int kb = 0; kb < NKS; ++kb) s = score_mfma(buf, kb, s);
     };
 
-    // keys past the end, and keys after the query under the causal mask, to -inf
+    // keys past the end, and keys after the query under the causal mask, to
+    // -inf.  Register r holds key kt*kBc + 8 lh + idx(r), idx(r) = 16 (r/8) +
+    // r%8, and a key is visible when it is at most the last key and (causal)
+    // the query row: one bound per lane, one compare with a constant per
+    // register.
     auto mask = [&](int kt, f32x16& s) {
-        const int key0 = kt * kBc;
+        const int last = CAUSAL ? min(qrow, a.Nk - 1) : a.Nk - 1;
+        const int lim = last - kt * kBc - 8 * lh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 16 * (r >> 3) + 8 * lh + (r & 7);
-            const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
-            s[r] = ok ? s[r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) s[r] = 16 * (r >> 3) + (r & 7) <= lim ? s[r] : -INFINITY;
     };
 
     // per-lane pieces of the transposing V read: row e of 4 (e = (lane%16)/4,
@@ -566,6 +567,8 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
         const float x = max16(A.s) * sl2;
         m = fmaxf(x, xor32(x));
     }
+    // minus the exponent base: the running maximum, or 0 while it is -inf;
+    // changes only where m does
 
     // Source order of one iteration: kSlots slots, each with one MFMA and a
     // share of the vector work (the compiler's scheduler takes it from there):
@@ -600,7 +603,7 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
         constexpr bool PREV = decltype(prev)::value;
         constexpr bool NEXT = decltype(next)::value;
         auto st = [&](int d) { return R >= 0 ? ((R + d) & (C::kStages - 1)) : stage_of(j + d); };
-        const float base = m == -INFINITY ? 0.f : m;
+        const float nbase = -(m == -INFINITY ? 0.f : m);
 
         bf16x8 ka[F8 ? 2 : NKB], va[kPairsV];
         if constexpr (NEXT) {
@@ -649,8 +652,8 @@ __device__ __forceinline__ void prefill_items(PrefillArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 if (pair_slot(k) == slot) {
-                    xs[2 * k] = fmaf(cur.s[2 * k], sl2, -base);
-                    xs[2 * k + 1] = fmaf(cur.s[2 * k + 1], sl2, -base);
+                    xs[2 * k] = fmaf(cur.s[2 * k], sl2, nbase);
+                    xs[2 * k + 1] = fmaf(cur.s[2 * k + 1], sl2, nbase);
                 }
                 if (pair_slot(k) + 1 == slot) {
                     xs[2 * k] = __builtin_amdgcn_exp2f(xs[2 * k]);

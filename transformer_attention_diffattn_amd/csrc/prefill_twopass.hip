@@ -363,14 +363,14 @@ __device__ __forceinline__ void twopass_items(const PrefillArgs& a) {
             (lds_s16x4*)(__attribute__((address_space(3))) uint8_t*)(vp + 4 * kVRow));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    // register r holds key kt*kBc + 8 lh + 16 (r/8) + r%8: one bound per lane
+    // (the last key, and under the causal mask the query row), one compare
+    // with a constant per register
     auto mask = [&](int kt, f32x16& s) {
-        const int key0 = kt * kBc;
+        const int last = CAUSAL ? min(qrow, a.Nk - 1) : a.Nk - 1;
+        const int lim = last - kt * kBc - 8 * lh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 16 * (r >> 3) + 8 * lh + (r & 7);
-            const bool ok = key < a.Nk && (!CAUSAL || key <= qrow);
-            s[r] = ok ? s[r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) s[r] = 16 * (r >> 3) + (r & 7) <= lim ? s[r] : -INFINITY;
     };
     // key tile of sequence entry s
     auto tile_of = [&](int s) { return s < nkt ? s : s - nkt; };
