@@ -49,6 +49,10 @@ template <>
 struct Chunk8<uint16_t> {
     u32x4 w;
     __device__ __forceinline__ void load(const uint16_t* p) { w = *(const u32x4*)p; }
+    // a cache row, read once per launch: streamed past the caches
+    __device__ __forceinline__ void stream(const uint16_t* p) {
+        w = __builtin_nontemporal_load((const u32x4*)p);
+    }
     __device__ __forceinline__ float get(int e) const {
         const uint32_t x = w[e >> 1];
         return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
@@ -61,6 +65,10 @@ struct Chunk8<float> {
     __device__ __forceinline__ void load(const float* p) {
         w0 = *(const u32x4*)p;
         w1 = *(const u32x4*)(p + 4);
+    }
+    __device__ __forceinline__ void stream(const float* p) {
+        w0 = __builtin_nontemporal_load((const u32x4*)p);
+        w1 = __builtin_nontemporal_load((const u32x4*)(p + 4));
     }
     __device__ __forceinline__ float get(int e) const {
         return __uint_as_float(e < 4 ? w0[e] : w1[e - 4]);
@@ -222,13 +230,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) 
 #pragma unroll
         for (int i = 0; i < C::kKLoads; ++i) {
             const int key = min(kbase + i * C::kKpi + lane / C::kLpk, last);
-            kc1[i].load(gk1 + (size_t)key * D + 8 * kch);
-            kc2[i].load(gk2 + (size_t)key * D + 8 * kch);
+            kc1[i].stream(gk1 + (size_t)key * D + 8 * kch);
+            kc2[i].stream(gk2 + (size_t)key * D + 8 * kch);
         }
 #pragma unroll
         for (int i = 0; i < C::kVLoads; ++i) {
             const int key = min(kbase + i * C::kRpi + vrow, last);
-            vc[i].load(gv + (size_t)key * DV + 8 * vch);
+            vc[i].stream(gv + (size_t)key * DV + 8 * vch);
         }
 
         // scores: in-lane partial dot products, summed over the key's lanes
