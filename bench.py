@@ -165,12 +165,13 @@ def measure_peaks():
     out["mfma_bf16_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
     # the shader clock the matrix cores ran at: 4096 bf16 flops per CU and cycle
     out["mfma_clock_ghz"] = round(flops / (ms * 1e-3) / (cus * 4096) / 1e9, 3)
-    # streaming reads of 4 GiB, each byte once
+    # streaming reads of 4 GiB, each byte once: 16 blocks per CU, each one
+    # contiguous 1 MiB piece
     nbytes = 4 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
-    rblocks = cus * 8
-    rsink = torch.empty(rblocks * 512, dtype=torch.int32, device="cuda")
+    rblocks = cus * 16
+    rsink = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
     ms = timed(lambda: lib.peaks_read_bw(src.data_ptr(), nbytes // 16, rsink.data_ptr(), rblocks,
                                          stream), reps=3)
     out["hbm_read_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
