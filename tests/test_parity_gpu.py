@@ -358,6 +358,27 @@ def test_decode_split_count_invariance():
     assert torch.equal(again, outs[2])
 
 
+# Decode's bitwise repeatability and no stray writes, with one split (the
+# epilogue in the partial kernel) and with four (partials, then the merge):
+# the output sits between two guard bands; 100 launches, identical bits.
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_deterministic_and_canary(splits):
+    w = _custom_decode(3, 5, 1000, 64, 128, "bf16", seed=41)
+    x = _to(workloads.make_decode(w, device="cpu"))
+    n = 3 * 5 * 128
+    guard = 4096
+    buf = torch.full((guard + n + guard,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[guard:guard + n].view(3, 5, 128)
+    da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], num_splits=splits, out=out)
+    first = out.clone()
+    for _ in range(100):
+        da.decode(x["q1"], x["q2"], x["k1"], x["k2"], x["v"], x["lam"], num_splits=splits,
+                  out=out)
+        assert torch.equal(out, first)
+    assert bool((buf[:guard] == 7.0).all()), "write before the output"
+    assert bool((buf[guard + n:] == 7.0).all()), "write past the output"
+
+
 def test_full_size_decode_sampled():
     w = workloads.get("decode_bf16")
     xg = workloads.make_decode(w, device=DEV)
