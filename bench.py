@@ -587,13 +587,16 @@ def main():
 
     mpk = measure_peaks() if "peaks" in legs else {}
 
-    # the other prefill workloads first (each with the same warm-up and step
-    # counts), then the headline
+    # the other prefill workloads first, then the headline.  A leg times at
+    # least 100 launches after at least 20 warm-up ones whatever --steps and
+    # --warmup say: 20 launches of the 2K workload span 2.4 ms, short enough
+    # for clock transitions to show in the figure (only the headline is tied
+    # to exactly --steps steps)
     prefill_legs = {}
     for name in ("large_head_bf16", "causal_prefill_bf16"):
         if name in legs and name != w.name:
             wl = workloads.get(name)
-            _, lms = bench_prefill(wl, args.steps, args.warmup, wall=False)
+            _, lms = bench_prefill(wl, max(args.steps, 100), max(args.warmup, 20), wall=False)
             prefill_legs[name] = prefill_record(wl, None, lms, mpk)
 
     wall_ms, kern_ms = bench_prefill(w, args.steps, args.warmup)
