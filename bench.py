@@ -433,7 +433,7 @@ def backward_record(w, args, mpk: dict) -> dict:
     """The backward leg on workload w: diffattn_bwd after the training
     forward, TFLOP/s at 12 d + 4 dv flops per unmasked (query, key) pair (the
     two score products again, dP, dV, dK_k and dQ_k)."""
-    bms, tfms = bench_backward(w, max(5, args.steps // 5), max(3, args.warmup // 20))
+    bms, tfms = bench_backward(w, max(20, args.steps // 5), max(5, args.warmup // 20))
     pairs = w.exec_flops() / (4 * (w.d + w.dv))
     bflops = pairs * (12 * w.d + 4 * w.dv)
     btf = bflops / (bms * 1e-3) / 1e12
@@ -458,7 +458,7 @@ def fp8_record(w, args, mpk: dict) -> dict:
     their time at the two peaks.  Per unmasked (query, key) pair the
     head_dim-128 kernel computes the scores twice (8 d flops: both maps, both
     sweeps) and one P.V of 2 dv; the head_dim-64 kernel 4 d and 4 dv."""
-    fms, bms16 = bench_fp8(w, max(10, args.steps // 3), max(20, args.warmup // 5))
+    fms, bms16 = bench_fp8(w, max(30, args.steps // 3), max(20, args.warmup // 5))
     f = w.exec_flops()
     pairs = f / (4 * (w.d + w.dv))
     sf, pf = (8 * w.d, 2 * w.dv) if w.d == 128 else (4 * w.d, 4 * w.dv)
@@ -634,7 +634,7 @@ def main():
     for leg, want in (("decode", 0), ("decode_split", DECODE_SPLITS)):
         if leg not in legs:
             continue
-        dms, splits, ws_bytes = bench_decode(wd, max(5, args.steps // 5), max(2, args.warmup // 10),
+        dms, splits, ws_bytes = bench_decode(wd, max(20, args.steps // 5), max(5, args.warmup // 10),
                                              splits=want)
         gbs = nbytes / (dms * 1e-3) / 1e9
         kern = "decode_partial_kernel" + (" + decode_merge_kernel" if splits > 1 else "")
@@ -664,7 +664,7 @@ def main():
             rec[key] = fp8_record(wf, args, mpk)
 
     if "proj" in legs:
-        pms, lms, pflops = bench_proj(w2, max(10, args.steps // 3), max(20, args.warmup // 3))
+        pms, lms, pflops = bench_proj(w2, max(30, args.steps // 3), max(20, args.warmup // 3))
         ptf = pflops / (pms * 1e-3) / 1e12
         rec["qkv_proj"] = {
             "workload": f"{w2.name} projections (d_model {w2.H * w2.dv})",
