@@ -438,6 +438,7 @@ def backward_record(w, args, mpk: dict) -> dict:
     bflops = pairs * (12 * w.d + 4 * w.dv)
     btf = bflops / (bms * 1e-3) / 1e12
     kern = ("bwd_prep + bwd_dq_ring + bwd_dkdv_ring + bwd_dlam" if w.d == 128
+            else "bwd_prep + bwd_dq + bwd_dkdv16 + bwd_dlam" if w.d == 64
             else "bwd_prep + bwd_dq + bwd_dkdv + bwd_dlam")
     return {
         "workload": w.name,

@@ -85,7 +85,7 @@ def entries():
          ("fp8_qk_large_head", "ms_per_call")),
         ("qkv_proj_kernel", "causal_prefill_bf16", "proj.hip", "b", ("qkv_proj", "ms_per_call")),
         ("bwd_dq_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
-        ("bwd_dkdv_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
+        ("bwd_dkdv16_kernel", "causal_prefill_bf16", "backward.hip+tile_ops.h", "b", None),
         ("bwd_dq_pair_kernel", "large_head_bf16", "backward_ring.hip+tile_ops.h", "b", None),
         ("bwd_dkdv_ring_kernel", "large_head_bf16", "backward_ring.hip+tile_ops.h", "b", None),
     ]
@@ -317,7 +317,7 @@ XCDS = 8
 # pair on the large-head one)
 BACKWARD_KERNELS = [
     ("bwd_dq_kernel", "causal_prefill_bf16"),
-    ("bwd_dkdv_kernel", "causal_prefill_bf16"),
+    ("bwd_dkdv16_kernel", "causal_prefill_bf16"),
     ("bwd_dq_pair_kernel", "large_head_bf16"),
     ("bwd_dkdv_ring_kernel", "large_head_bf16"),
 ]

@@ -25,8 +25,10 @@
 //          over key tiles; dQ_k = tau (X_k - delta_k Y_k) with X_k = (A_k * dP)
 //          K_k and Y_k = A_k K_k, so delta_k comes out of the same sweep;
 //          writes dQ and delta_k;
-//   dkdv   a workgroup per 128 keys (wave = 32 keys, both maps), looping over
-//          query tiles; accumulates dV^T and dK_k^T;
+//   dkdv   a workgroup per 128 keys, looping over query tiles; head_dim 32:
+//          wave = 32 keys and both maps, accumulating dV^T and dK_k^T on
+//          32x32x16 products; head_dim 64 (dkdv16): wave = 16 keys and both
+//          maps on 16x16x32 products, two waves per SIMD;
 //   dlam   one workgroup per head: dlambda = -sum delta_2 (fixed order).
 //
 // MFMA v_mfma_f32_32x32x16_bf16 throughout (lane l, lh = l / 32, l32 = l % 32:
@@ -483,6 +485,251 @@ void bwd_dkdv_kernel(BackwardArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dkdv16: the dkdv products for head_dim 64 on v_mfma_f32_16x16x32_bf16, 16
+// keys per wave, so that a wave holds half the key-side state of bwd_dkdv and
+// two waves share each SIMD.  Workgroup = 128 keys of one (b, h), 8 waves;
+// wave w owns keys 16 w .. 16 w + 15 and both maps.
+//
+// 16x16x32 operands (lane l, g = l / 16, i = l % 16): A row i and B column i
+// hold k-slots 8 g .. 8 g + 7; accumulator register r is row 4 g + r, column i.
+// Per 32-query tile, in two blocks b of 16 queries:
+//   S_k^T[b] = Q_k[b] K_k^T,   dP^T[b] = dD[b] V^T          (queries x keys)
+// so lane l holds key i of the wave and queries 16 b + 4 g + r: the eight
+// queries 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, which serve as lane
+// group g's k-slots in
+//   dV += W dD,   dK_k += dS_k Q_k                          (keys x channels)
+// whose A operands are the weights already in registers and whose B operands
+// (columns of dD and Q_k over those queries) come from two transposing reads
+// of four rows each.
+// The LDS tiles are unpadded; chunk c (16 bytes) of row r sits at c ^ swz16(r),
+// which puts both the row reads (16 rows at one chunk) and the transposing
+// reads (8 rows by two chunks per half-wave) on 64 distinct banks.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ int swz16(int r) {
+    static_assert(W == 64 || W == 128, "rows of 128 or 256 bytes");
+    if constexpr (W == 128)
+        return 2 * (r & 7) + ((r >> 3) & 1);
+    else
+        return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// chunk c of row r of a swizzled tile of W-element rows
+template <int W>
+__device__ __forceinline__ bf16x8 rd_chunk(const uint16_t* t, int r, int c) {
+    return *(const bf16x8*)(t + r * W + 8 * (c ^ swz16<W>(r)));
+}
+
+// B operand over queries 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, column
+// c0 + i: lane i of a 16-lane group addresses row (i / 4) of its four rows at
+// columns c0 + 4 (i % 4) ..  and receives column c0 + i of the four rows
+template <int W>
+__device__ __forceinline__ bf16x8 rd_qcol(const uint16_t* t, int c0, int lane) {
+    const int g = lane >> 4, e = (lane & 15) >> 2, col = c0 + 4 * (lane & 3);
+    const int r0 = 4 * g + e, r1 = 16 + 4 * g + e;
+    const uint16_t* p0 = t + r0 * W + 8 * ((col >> 3) ^ swz16<W>(r0)) + (col & 7);
+    const uint16_t* p1 = t + r1 * W + 8 * ((col >> 3) ^ swz16<W>(r1)) + (col & 7);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+constexpr int kKv16Threads = 512;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kKv16Threads) void bwd_dkdv16_kernel(BackwardArgs a) {
+    constexpr int D = 64, DV = 128;
+    constexpr int NS = D / 32, NSV = DV / 32;   // k-steps over d and over dv
+    constexpr int NC = D / 16, NCV = DV / 16;   // 16-channel output blocks
+    // two buffers, each Q1 | Q2 | dD of one 32-query tile and its row terms
+    __shared__ __attribute__((aligned(16))) uint16_t sq[2][2][32 * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sd[2][32 * DV];
+    // per query: lse1, lse2 (log2 units), delta1, delta2
+    __shared__ __attribute__((aligned(16))) float4 srow[2][32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, i16 = lane & 15;
+    const int BH = a.B * a.H;
+    // key tile kt = blockIdx / BH: under the causal mask the first key tiles
+    // see the most queries, so the longest workgroups start first
+    const int kt = blockIdx.x / BH;
+    const int bh = blockIdx.x - kt * BH;
+    const int h = bh % a.H;
+    const int kw0 = kt * 128 + 16 * wave;  // first key of this wave
+    const int key = kw0 + i16;             // this lane's key (column i)
+    const bool kok = key < a.Nk;
+
+    const uint16_t* gk1 = (const uint16_t*)a.k1 + (size_t)bh * a.Nk * D;
+    const uint16_t* gk2 = (const uint16_t*)a.k2 + (size_t)bh * a.Nk * D;
+    const uint16_t* gv = (const uint16_t*)a.v + (size_t)bh * a.Nk * DV;
+    const uint16_t* gq1 = (const uint16_t*)a.q1 + (size_t)bh * a.Nq * D;
+    const uint16_t* gq2 = (const uint16_t*)a.q2 + (size_t)bh * a.Nq * D;
+    const uint16_t* gdd = (const uint16_t*)a.dd + (size_t)bh * a.Nq * DV;
+
+    // B operands of this lane's key: K_k^T and V^T, k-step s = channels 32 s + 8 g ..
+    bf16x8 k1f[NS], k2f[NS], vf[NSV];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        k1f[s] = kok ? *(const bf16x8*)(gk1 + (size_t)key * D + 32 * s + 8 * g) : bf16x8{};
+        k2f[s] = kok ? *(const bf16x8*)(gk2 + (size_t)key * D + 32 * s + 8 * g) : bf16x8{};
+    }
+#pragma unroll
+    for (int s = 0; s < NSV; ++s)
+        vf[s] = kok ? *(const bf16x8*)(gv + (size_t)key * DV + 32 * s + 8 * g) : bf16x8{};
+    const float sl2 = a.scale_log2;
+    const float lam = a.lam[h];
+
+    f32x4 dvv[NCV], dk1[NC], dk2[NC];
+#pragma unroll
+    for (int c = 0; c < NCV; ++c) dvv[c] = f32x4{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) dk1[c] = dk2[c] = f32x4{};
+
+    const int nqt = (a.Nq + 31) / 32;
+    const int qt0 = CAUSAL ? (kt * 128) / 32 : 0;
+    const float* lse1 = a.lse + (size_t)bh * a.Nq;
+    const float* lse2 = a.lse + ((size_t)BH + bh) * a.Nq;
+    const float* del1 = a.delta + (size_t)bh * a.Nq;
+    const float* del2 = a.delta + ((size_t)BH + bh) * a.Nq;
+    // row terms: thread t < 128 carries term t / 32 of query t % 32
+    const int which = tid >> 5;
+    const float row_scale = which < 2 ? kLog2e : 1.f;  // log-sum-exps to log2 units
+    const float* rsrc = which == 0 ? lse1 : which == 1 ? lse2 : which == 2 ? del1 : del2;
+    // tile chunks: thread t moves chunk t of Q1 | Q2 (t < 256: Q1) and chunk t of dD
+    const int qsel = __builtin_amdgcn_readfirstlane(tid >> 8), qc = tid & 255;  // uniform per wave
+    const int q_row = qc >> 3, q_ch = qc & 7;
+    const int d_row = tid >> 4, d_ch = tid & 15;
+    uint4 rq, rd;
+    float rv = 0.f;
+    // rows past Nq read as zeros (buffer bounds) and, for the row terms, as the
+    // last row's (an index clamp); their pairs are masked
+    auto load_tile = [&](int qt) {
+        const int64_t row0 = (int64_t)qt * 32;
+        const __amdgpu_buffer_rsrc_t rs_q =
+            buffer_rsrc((qsel ? gq2 : gq1) + row0 * D, ((int64_t)a.Nq - row0) * D * 2);
+        const __amdgpu_buffer_rsrc_t rs_d = buffer_rsrc(gdd + row0 * DV, ((int64_t)a.Nq - row0) * DV * 2);
+        rq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs_q, (q_row * D + 8 * q_ch) * 2, 0, 0));
+        rd = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs_d, (d_row * DV + 8 * d_ch) * 2, 0, 0));
+        if (tid < 128) rv = rsrc[min(qt * 32 + (tid & 31), a.Nq - 1)];
+    };
+    auto store_tile = [&](int b) {
+        *(uint4*)(&sq[b][qsel][q_row * D + 8 * (q_ch ^ swz16<D>(q_row))]) = rq;
+        *(uint4*)(&sd[b][d_row * DV + 8 * (d_ch ^ swz16<DV>(d_row))]) = rd;
+        if (tid < 128) ((float*)&srow[b][tid & 31])[which] = rv * row_scale;
+    };
+    if (qt0 < nqt) {
+        load_tile(qt0);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; ++qt) {
+        const int buf = (qt - qt0) & 1;
+        const bool more = qt + 1 < nqt;
+        if (more) load_tile(qt + 1);  // in flight while this tile is used
+        const uint16_t* sq1 = sq[buf][0];
+        const uint16_t* sq2 = sq[buf][1];
+        const uint16_t* sd_ = sd[buf];
+        const float4* sr = srow[buf];
+
+        // S_k^T and dP^T, query block b: A rows 16 b + i, chunk 4 s + g
+        f32x4 s1[2], s2[2], dp[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            s1[b] = s2[b] = dp[b] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                s1[b] = mfma16(rd_chunk<D>(sq1, 16 * b + i16, 4 * s + g), k1f[s], s1[b]);
+                s2[b] = mfma16(rd_chunk<D>(sq2, 16 * b + i16, 4 * s + g), k2f[s], s2[b]);
+            }
+#pragma unroll
+            for (int s = 0; s < NSV; ++s)
+                dp[b] = mfma16(rd_chunk<DV>(sd_, 16 * b + i16, 4 * s + g), vf[s], dp[b]);
+        }
+        // the B operands of the dV and dK products (independent of the vector
+        // work below), in flight meanwhile
+        bf16x8 bd[NCV], bq1[NC], bq2[NC];
+#pragma unroll
+        for (int c = 0; c < NCV; ++c) bd[c] = rd_qcol<DV>(sd_, 16 * c, lane);
+        // weights; the mask only where the tile meets the diagonal or an end
+        const bool full = __builtin_amdgcn_readfirstlane(kw0) + 15 < a.Nk && qt * 32 + 31 < a.Nq &&
+                          (!CAUSAL || __builtin_amdgcn_readfirstlane(kw0) + 15 <= qt * 32);
+        bf16x8 wa, da1, da2;
+        auto probs = [&](auto masked) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = 16 * b + 4 * g + r;
+                    const float4 t = sr[qi];
+                    float x1 = fmaf(s1[b][r], sl2, -t.x), x2 = fmaf(s2[b][r], sl2, -t.y);
+                    if constexpr (decltype(masked)::value) {
+                        const int q = qt * 32 + qi;
+                        const bool ok = kok && q < a.Nq && (!CAUSAL || key <= q);
+                        asm volatile("" : "+v"(x1), "+v"(x2));
+                        x1 = ok ? x1 : -INFINITY;
+                        x2 = ok ? x2 : -INFINITY;
+                    }
+                    const float p1 = __builtin_amdgcn_exp2f(x1);
+                    const float p2 = __builtin_amdgcn_exp2f(x2);
+                    wa[4 * b + r] = (__bf16)(p1 - lam * p2);
+                    da1[4 * b + r] = (__bf16)(p1 * (dp[b][r] - t.z));
+                    da2[4 * b + r] = (__bf16)(-lam * p2 * (dp[b][r] - t.w));
+                }
+            }
+        };
+        if (full)
+            probs(std::false_type{});
+        else
+            probs(std::true_type{});
+        // dV += W dD, dK_k += dS_k Q_k (k = the eight queries of lane group g)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            bq1[c] = rd_qcol<D>(sq1, 16 * c, lane);
+            bq2[c] = rd_qcol<D>(sq2, 16 * c, lane);
+        }
+#pragma unroll
+        for (int c = 0; c < NCV; ++c) dvv[c] = mfma16(wa, bd[c], dvv[c]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            dk1[c] = mfma16(da1, bq1[c], dk1[c]);
+            dk2[c] = mfma16(da2, bq2[c], dk2[c]);
+        }
+        // the other buffer was last read before the previous barrier
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // accumulator register r of block c: key kw0 + 4 g + r, channel 16 c + i
+    const float tau = 1.f / sqrtf((float)D);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int kr = kw0 + 4 * g + r;
+        if (kr >= a.Nk) continue;
+        __bf16* o1 = (__bf16*)a.dk1 + ((size_t)bh * a.Nk + kr) * D;
+        __bf16* o2 = (__bf16*)a.dk2 + ((size_t)bh * a.Nk + kr) * D;
+        __bf16* ov = (__bf16*)a.dv + ((size_t)bh * a.Nk + kr) * DV;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            o1[16 * c + i16] = (__bf16)(tau * dk1[c][r]);
+            o2[16 * c + i16] = (__bf16)(tau * dk2[c][r]);
+        }
+#pragma unroll
+        for (int c = 0; c < NCV; ++c) ov[16 * c + i16] = (__bf16)dvv[c][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dlam: dlambda_h = -sum over batch and rows of delta_2 (fixed order)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads) void bwd_dlam_kernel(BackwardArgs a) {
@@ -529,9 +776,14 @@ hipError_t launch_dims(const BackwardArgs& a, bool causal, hipStream_t stream) {
                                : (const void*)bwd_dq_kernel<D, DV, false>,
                         dim3((unsigned)g_dq), dim3(kBwdThreads), args, 0, stream);
     if (e != hipSuccess) return e;
-    e = hipLaunchKernel(causal ? (const void*)bwd_dkdv_kernel<D, DV, true>
-                               : (const void*)bwd_dkdv_kernel<D, DV, false>,
-                        dim3((unsigned)g_kv), dim3(kBwdThreads), args, 0, stream);
+    if constexpr (D == 64 && DV == 128)
+        e = hipLaunchKernel(causal ? (const void*)bwd_dkdv16_kernel<true>
+                                   : (const void*)bwd_dkdv16_kernel<false>,
+                            dim3((unsigned)g_kv), dim3(kKv16Threads), args, 0, stream);
+    else
+        e = hipLaunchKernel(causal ? (const void*)bwd_dkdv_kernel<D, DV, true>
+                                   : (const void*)bwd_dkdv_kernel<D, DV, false>,
+                            dim3((unsigned)g_kv), dim3(kBwdThreads), args, 0, stream);
     if (e != hipSuccess) return e;
     return hipLaunchKernel((const void*)bwd_dlam_kernel, dim3((unsigned)a.H), dim3(kBwdThreads),
                            args, 0, stream);
