@@ -194,6 +194,49 @@ def test_backward_deterministic(d, dv):
         assert torch.equal(ga, gb)
 
 
+# No stray writes: every gradient goes into the middle of a guard-banded
+# buffer through the C ABI, with ragged query and key counts (333 = 2 x 128 +
+# 77 keys, 10 x 32 + 13 queries); the results equal the binding's and the
+# bands stay untouched.
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("d,dv", DIMS, ids=DIM_IDS)
+def test_backward_canary(d, dv, causal):
+    import ctypes
+    w, x, dout = _inputs(1, 3, 333, d, dv, causal, seed=97)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    dout = dout.cuda()
+    out, d_save, lse = da.fwd_train(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"],
+                                    causal=causal)
+    ref = da.bwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"], g["lam"], dout, d_save, lse,
+                 causal=causal)
+    guard = 2048
+    bufs, views = [], []
+    for t in (g["q1"], g["q2"], g["k1"], g["k2"], g["v"]):
+        b = torch.full((guard + t.numel() + guard,), 7.0, dtype=t.dtype, device=t.device)
+        bufs.append(b)
+        views.append(b[guard:guard + t.numel()].view(t.shape))
+    dl_buf = torch.full((guard + 3 + guard,), 7.0, dtype=torch.float32, device="cuda")
+    dlam = dl_buf[guard:guard + 3]
+    B, H, N = 1, 3, 333
+    dims = da.Dims(B, H, N, N, d, dv, da._dtype_code(g["q1"]), 1e-5, da._flags(False, False))
+    need = int(da.lib().diffattn_bwd_workspace_size(ctypes.byref(dims)))
+    ws = torch.empty((max(need, 16),), dtype=torch.uint8, device="cuda")
+    lam_t = da._lam_tensor(g["lam"], H, g["q1"].device)
+    st = da.lib().diffattn_bwd(g["q1"].data_ptr(), g["q2"].data_ptr(), g["k1"].data_ptr(),
+                               g["k2"].data_ptr(), g["v"].data_ptr(), lam_t.data_ptr(), 0.8,
+                               int(causal), dout.data_ptr(), d_save.data_ptr(), lse.data_ptr(),
+                               *[v_.data_ptr() for v_ in views], dlam.data_ptr(), ws.data_ptr(),
+                               ws.numel(), ctypes.byref(dims), da._stream_ptr(g["q1"].device))
+    assert st == 0, st
+    torch.cuda.synchronize()
+    for name, got, want, b in zip(("dq1", "dq2", "dk1", "dk2", "dv"), views, ref[:5], bufs):
+        assert torch.equal(got, want), name
+        assert bool((b[:guard] == 7.0).all()), f"{name}: write before the output"
+        assert bool((b[guard + got.numel():] == 7.0).all()), f"{name}: write past the output"
+    assert torch.equal(dlam, ref[5])
+    assert bool((dl_buf[:guard] == 7.0).all()) and bool((dl_buf[guard + 3:] == 7.0).all())
+
+
 def test_backward_rejects_unsupported_and_small_workspace():
     w, x, dout = _inputs(1, 1, 16, 32, 128, True, seed=94)
     g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
