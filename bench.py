@@ -135,7 +135,8 @@ def _peaks_lib():
     lib.peaks_mfma_bf16.argtypes = [vp, i32, i32, vp]
     lib.peaks_read_bw.argtypes = [vp, i64, vp, i32, vp]
     lib.peaks_vector_rate.argtypes = [vp, i32, i32, i32, vp]
-    for f in (lib.peaks_mfma_bf16, lib.peaks_read_bw, lib.peaks_vector_rate,
+    lib.peaks_lds_read.argtypes = [vp, i32, i32, vp]
+    for f in (lib.peaks_mfma_bf16, lib.peaks_read_bw, lib.peaks_vector_rate, lib.peaks_lds_read,
               lib.peaks_mfma_chains, lib.peaks_vector_chains):
         f.restype = ctypes.c_int
     return lib
@@ -183,8 +184,16 @@ def measure_peaks():
         ms = timed(lambda: lib.peaks_vector_rate(sink.data_ptr(), vblocks, viters, use_fma, stream))
         rate = per / (ms * 1e-3)
         out[f"v_{name}_f32_per_cu_clk"] = round(rate / cus / (out["mfma_clock_ghz"] * 1e9), 2)
-    out["note"] = ("lanes per CU and shader cycle, at the clock the MFMA test ran at; "
-                   "v_fma_f32 counts one instruction per lane")
+    # LDS reads: two workgroups of 16 waves per CU, 64 KB each
+    lblocks, liters = cus * 2, 2048
+    lsink = torch.empty(lblocks * 1024, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: lib.peaks_lds_read(lsink.data_ptr(), lblocks, liters, stream))
+    lbytes = lblocks * 1024 * liters * 8 * 16
+    out["lds_read_gbs_per_cu"] = round(lbytes / (ms * 1e-3) / 1e9 / cus, 1)
+    out["lds_read_bytes_per_cu_clk"] = round(lbytes / (ms * 1e-3) / cus / (out["mfma_clock_ghz"] * 1e9), 1)
+    del lsink
+    out["note"] = ("lanes (LDS: bytes) per CU and shader cycle, at the clock the MFMA test ran "
+                   "at; v_fma_f32 counts one instruction per lane")
     del sink
     torch.cuda.empty_cache()
     return out

@@ -8,6 +8,9 @@
 //                     16-byte non-temporal loads, each byte once (on MI355X
 //                     this pattern reads ~7.1 TB/s where a grid-stride walk
 //                     over the same buffer, or plain loads, stay near 6.3);
+//   peaks_lds_read    LDS read rate: 16 waves per workgroup stream
+//                     conflict-free 16-byte reads over 64 KB of LDS (the
+//                     attention kernels' operand path);
 //   peaks_exp_rate    v_exp_f32 throughput (the softmax's transcendental),
 //                     independent chains in every lane; and the same for
 //                     v_fma_f32, so the two can be compared.
@@ -76,6 +79,30 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
     if (acc == 0x9e3779b9u) sink[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// every lane: 8 independent 16-byte reads per step; 16 consecutive lanes read
+// 256 contiguous bytes (all 64 banks once).  Each address passes through an
+// empty asm, so the compiler cannot reuse a load of an earlier step (7 of a
+// step's 8 addresses recur in the next), and all four words are used, so
+// each read stays 16 bytes wide.
+__global__ __launch_bounds__(1024) void lds_read_kernel(uint32_t* sink, int iters) {
+    __shared__ __attribute__((aligned(16))) uint8_t buf[65536];
+    for (int i = threadIdx.x; i < 65536 / 16; i += blockDim.x)
+        ((u32x4*)buf)[i] = u32x4{(uint32_t)i, (uint32_t)i + 1, (uint32_t)i + 2, (uint32_t)i + 3};
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            int off = ((wave * 8 + u + it) * 1024 + lane * 16) & 65535;
+            asm volatile("" : "+v"(off));
+            const u32x4 v = *(const u32x4*)(buf + off);
+            acc += (v[0] ^ v[1]) + (v[2] ^ v[3]);
+        }
+    }
+    if (acc == 0x12345u) sink[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 constexpr int kExpChains = 8;
 
 // x <- 2^-x keeps every chain in [0.5, 1]: the negation is a source modifier
@@ -126,6 +153,14 @@ int peaks_mfma_bf16(void* sink, int blocks, int iters, void* stream) {
 int peaks_read_bw(const void* src, int64_t n16, void* sink, int blocks, void* stream) {
     hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                        (const u32x4*)src, n16, (uint32_t*)sink);
+    return (int)hipGetLastError();
+}
+
+// LDS bytes read by one launch: blocks * 1024 * iters * 8 * 16.
+// sink: blocks * 1024 uint32 of device memory.
+int peaks_lds_read(void* sink, int blocks, int iters, void* stream) {
+    hipLaunchKernelGGL(lds_read_kernel, dim3(blocks), dim3(1024), 0, (hipStream_t)stream,
+                       (uint32_t*)sink, iters);
     return (int)hipGetLastError();
 }
 
